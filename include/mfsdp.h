@@ -1,0 +1,177 @@
+/*
+ * mfsdp.h - C ABI of the owner-local Muon + AdamW optimizer step (gfx950).
+ *
+ * What it computes.  "MatrixFSDP: Communication-Free Matrix Optimizers Under
+ * ZeRO-3 Parameter Sharding" (arXiv 2607.05895), Abstract and §1: under
+ * owner-shaped sharding one data-parallel rank holds every 2D weight whole,
+ * so Muon's Newton-Schulz orthogonalisation runs locally on that owner, and
+ * the non-matrix tensors packed into tail owners stay on AdamW.  The result
+ * must equal full-matrix Muon on the gathered matrix (Abstract; §1).  This
+ * library is that owner-local step for one GPU: a table of whole tensors
+ * (offsets, shapes, dtypes, roles; the paper's MatrixShard metadata, Abstract)
+ * that live in one flat parameter buffer, and one call that updates all of
+ * them.
+ *
+ * Per Muon matrix W (rows x cols), gradient G, fp32 momentum M:
+ *   M <- beta*M + G;  U <- G + beta*M (Nesterov) or U <- M;
+ *   X <- U / (||U||_F + eps), taken in the wide orientation (tall -> U^T);
+ *   ns_steps times: A = X X^T;  B = b*A + c*A*A;  X <- a*X + B*X;
+ *   O = X back in W's orientation;
+ *   W <- W*(1 - lr*weight_decay) - lr*scale*O,
+ *   scale = sqrt(max(1, rows/cols)) (mode 0) or 0.2*sqrt(max(rows, cols)) (mode 1).
+ * Per AdamW tail tensor (1-based step t):
+ *   m <- b1*m + (1-b1)*g;  v <- b2*v + (1-b2)*g^2;
+ *   W <- W*(1 - lr_a*wd_a) - lr_a*(m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps_a).
+ * Every stored value is rounded once to its storage type, to nearest-even.
+ *
+ * Ownership.  The caller allocates every device buffer (params, grads,
+ * state, workspace, ns_out).  The library never allocates device memory.
+ * A plan is host memory owned by the library until mfsdp_plan_destroy.
+ *
+ * Errors.  Every function returns mfsdp_status; no C++ exception crosses the
+ * boundary and nothing aborts the process.  mfsdp_last_error_message()
+ * returns a thread-local description of the last failure on this thread.
+ */
+#ifndef MFSDP_H
+#define MFSDP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mfsdp_status {
+    MFSDP_OK = 0,
+    MFSDP_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad step, out of range */
+    MFSDP_ERR_OVERLAP = 2,            /* two table entries share parameter bytes */
+    MFSDP_ERR_MISALIGNED = 3,         /* entry offset not a multiple of 16 bytes */
+    MFSDP_ERR_UNSUPPORTED = 4,        /* dtype, role, precision or dimension not supported */
+    MFSDP_ERR_WORKSPACE_TOO_SMALL = 5,/* workspace_bytes below mfsdp_plan_workspace_bytes */
+    MFSDP_ERR_HIP = 6,                /* a HIP runtime call or kernel launch failed */
+    MFSDP_ERR_INTERNAL = 7
+} mfsdp_status;
+
+typedef enum mfsdp_dtype {
+    MFSDP_F32 = 0,
+    MFSDP_BF16 = 1
+} mfsdp_dtype;
+
+typedef enum mfsdp_role {
+    MFSDP_ROLE_AUTO = 0,   /* Muon iff rows > 1 and cols > 1, else AdamW */
+    MFSDP_ROLE_MUON = 1,   /* force Muon (rows >= 1, cols >= 1) */
+    MFSDP_ROLE_ADAMW = 2   /* force AdamW */
+} mfsdp_role;
+
+/* One whole tensor of the owner buffer (one row of the owner table).
+ * offset: byte offset into the params buffer; the grads buffer uses the same
+ *         offset.  Must be a multiple of 16.
+ * rows, cols: logical shape, row-major.  A 1D tensor of length L is rows=1,
+ *         cols=L.  rows*cols == 0 is an empty shard: legal and skipped.
+ * dtype:  storage type of both the parameter and its gradient.
+ * role:   mfsdp_role. */
+typedef struct mfsdp_entry {
+    uint64_t offset;
+    int64_t rows;
+    int64_t cols;
+    int32_t dtype;
+    int32_t role;
+} mfsdp_entry;
+
+/* Hyper-parameters.  Floats are used as the float32 values given. */
+typedef struct mfsdp_hparams {
+    float lr;                 /* Muon learning rate */
+    float weight_decay;       /* Muon decoupled weight decay (multiplied by lr) */
+    float momentum;           /* beta */
+    int32_t nesterov;         /* 1: U = G + beta*M; 0: U = M */
+    int32_t ns_steps;         /* Newton-Schulz iterations, 0..64 */
+    float ns_a, ns_b, ns_c;   /* quintic coefficients */
+    float ns_eps;             /* added to ||U||_F */
+    int32_t lr_scale_mode;    /* 0: sqrt(max(1, rows/cols)); 1: 0.2*sqrt(max(rows, cols)) */
+    int32_t ns_precision;     /* 0: bf16 operands, fp32 accumulate; 1: fp32 operands and accumulate */
+    float adam_lr;
+    float adam_beta1;
+    float adam_beta2;
+    float adam_eps;
+    float adam_weight_decay;
+} mfsdp_hparams;
+
+typedef struct mfsdp_plan_s* mfsdp_plan_t;
+
+/* Per-entry layout facts a caller needs to read or seed state. */
+typedef struct mfsdp_entry_info {
+    int32_t role;             /* resolved: MFSDP_ROLE_MUON, MFSDP_ROLE_ADAMW, or -1 for an empty entry */
+    int32_t transposed;       /* Muon: 1 if rows > cols (Newton-Schulz runs on the transpose) */
+    int64_t m, n;             /* Muon: oriented shape, m = min(rows, cols) */
+    uint64_t state_offset;    /* Muon: fp32 momentum; AdamW: fp32 first moment (bytes into state) */
+    uint64_t state_offset2;   /* AdamW: fp32 second moment (bytes into state); 0 otherwise */
+    uint64_t ns_out_offset;   /* Muon: element offset of the fp32 O export in ns_out */
+    float lr_scale;           /* Muon: the shape scale applied to lr */
+} mfsdp_entry_info;
+
+/* Step flags. */
+#define MFSDP_STEP_DESCRIPTORS_RESIDENT 1u  /* the workspace already holds this plan's
+                                               descriptors from an earlier step with the
+                                               same workspace pointer; skip the upload */
+
+typedef struct mfsdp_step_args {
+    void* params;             /* device, updated in place */
+    const void* grads;        /* device, read only; same offsets as params */
+    void* state;              /* device, mfsdp_plan_state_bytes, zero-filled before step 1 */
+    void* workspace;          /* device, mfsdp_plan_workspace_bytes, 256-byte aligned;
+                                 library scratch: the caller must not write it between steps */
+    uint64_t workspace_bytes;
+    int64_t step;             /* 1-based step count (AdamW bias correction) */
+    void* stream;             /* hipStream_t; NULL = the null stream */
+    float* ns_out;            /* NULL, or device fp32 [mfsdp_plan_ns_out_elems]: O per Muon entry,
+                                 row-major in the entry's own shape, at entry_info.ns_out_offset */
+    uint32_t flags;           /* MFSDP_STEP_* */
+} mfsdp_step_args;
+
+/* Validate an owner table and lower it to a plan (host only; no HIP call).
+ * entries: n rows (may be NULL when n == 0).  param_bytes: size of the params
+ * buffer, used for bounds checks.  hp: copied into the plan.
+ * Errors: INVALID_ARGUMENT (null pointer, n < 0, negative dim, entry past
+ * param_bytes, bad hyper-parameter), OVERLAP, MISALIGNED, UNSUPPORTED (dtype,
+ * role, ns_precision, a dimension above 2^22).  *out is set only on success. */
+mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n, uint64_t param_bytes,
+                               const mfsdp_hparams* hp, mfsdp_plan_t* out);
+
+/* Bytes of optimizer state the plan lays out (fp32 momentum for Muon entries,
+ * then fp32 first and second moments for AdamW entries). */
+mfsdp_status mfsdp_plan_state_bytes(mfsdp_plan_t plan, uint64_t* bytes);
+
+/* Bytes of device workspace one step needs (descriptors, norm partials,
+ * Newton-Schulz buffers). */
+mfsdp_status mfsdp_plan_workspace_bytes(mfsdp_plan_t plan, uint64_t* bytes);
+
+/* Number of fp32 elements of the optional ns_out export. */
+mfsdp_status mfsdp_plan_ns_out_elems(mfsdp_plan_t plan, uint64_t* elems);
+
+/* Number of table entries and the layout facts of entry i. */
+mfsdp_status mfsdp_plan_num_entries(mfsdp_plan_t plan, int64_t* n);
+mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsdp_entry_info* info);
+
+/* One owner step: enqueue every kernel on args->stream and return without
+ * synchronising.  Launch failures return MFSDP_ERR_HIP; a fault inside a
+ * kernel surfaces at the caller's next synchronisation.  One plan serves one
+ * stream at a time; two steps that share a workspace must not overlap.
+ * Errors: INVALID_ARGUMENT (null plan or args, null buffer needed by the
+ * table, step < 1 with an AdamW entry, misaligned workspace),
+ * WORKSPACE_TOO_SMALL, HIP. */
+mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args);
+
+/* Free a plan.  NULL is accepted. */
+mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
+
+/* Static description of a status code. */
+const char* mfsdp_status_string(mfsdp_status status);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* mfsdp_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFSDP_H */

@@ -1,0 +1,194 @@
+"""ctypes binding of libmfsdp.so (the C ABI in include/mfsdp.h).
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+library.  Buffers are passed as integer device addresses (for a torch
+tensor, ``t.data_ptr()``); streams as integer ``hipStream_t`` handles (for
+torch, ``torch.cuda.current_stream().cuda_stream``).  If the library has not
+been built, loading raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmfsdp.so")
+
+F32, BF16 = 0, 1
+ROLE_AUTO, ROLE_MUON, ROLE_ADAMW = 0, 1, 2
+STEP_DESCRIPTORS_RESIDENT = 1
+
+STATUS = {
+    0: "MFSDP_OK",
+    1: "MFSDP_ERR_INVALID_ARGUMENT",
+    2: "MFSDP_ERR_OVERLAP",
+    3: "MFSDP_ERR_MISALIGNED",
+    4: "MFSDP_ERR_UNSUPPORTED",
+    5: "MFSDP_ERR_WORKSPACE_TOO_SMALL",
+    6: "MFSDP_ERR_HIP",
+    7: "MFSDP_ERR_INTERNAL",
+}
+
+
+class Entry(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("role", ctypes.c_int32)]
+
+
+class Hparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float), ("momentum", ctypes.c_float),
+        ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+        ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float), ("ns_eps", ctypes.c_float),
+        ("lr_scale_mode", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
+        ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
+        ("adam_eps", ctypes.c_float), ("adam_weight_decay", ctypes.c_float),
+    ]
+
+
+class EntryInfo(ctypes.Structure):
+    _fields_ = [("role", ctypes.c_int32), ("transposed", ctypes.c_int32), ("m", ctypes.c_int64),
+                ("n", ctypes.c_int64), ("state_offset", ctypes.c_uint64), ("state_offset2", ctypes.c_uint64),
+                ("ns_out_offset", ctypes.c_uint64), ("lr_scale", ctypes.c_float)]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64), ("step", ctypes.c_int64),
+                ("stream", ctypes.c_void_p), ("ns_out", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+
+
+EXPORTS = (
+    "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
+    "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
+    "mfsdp_status_string", "mfsdp_last_error_message",
+)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmfsdp.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m matrix_optimizer_owner_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.mfsdp_plan_create.argtypes = [ctypes.POINTER(Entry), ctypes.c_int64, ctypes.c_uint64,
+                                      ctypes.POINTER(Hparams), ctypes.POINTER(P)]
+    lib.mfsdp_plan_state_bytes.argtypes = [P, u64p]
+    lib.mfsdp_plan_workspace_bytes.argtypes = [P, u64p]
+    lib.mfsdp_plan_ns_out_elems.argtypes = [P, u64p]
+    lib.mfsdp_plan_num_entries.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.mfsdp_plan_entry_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(EntryInfo)]
+    lib.mfsdp_owner_step.argtypes = [P, ctypes.POINTER(StepArgs)]
+    lib.mfsdp_plan_destroy.argtypes = [P]
+    lib.mfsdp_status_string.argtypes = [ctypes.c_int]
+    lib.mfsdp_status_string.restype = ctypes.c_char_p
+    lib.mfsdp_last_error_message.argtypes = []
+    lib.mfsdp_last_error_message.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("mfsdp_status_string", "mfsdp_last_error_message"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class MfsdpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().mfsdp_last_error_message().decode()
+        raise MfsdpError(status, msg)
+
+
+def make_hparams(**kw) -> Hparams:
+    """Hyper-parameters with Muon/AdamW defaults; keyword overrides."""
+    d = dict(lr=0.02, weight_decay=0.01, momentum=0.95, nesterov=1, ns_steps=5, ns_a=3.4445, ns_b=-4.7750,
+             ns_c=2.0315, ns_eps=1e-7, lr_scale_mode=0, ns_precision=0, adam_lr=0.02, adam_beta1=0.9,
+             adam_beta2=0.95, adam_eps=1e-8, adam_weight_decay=0.01)
+    unknown = set(kw) - set(d)
+    if unknown:
+        raise KeyError(f"unknown hyper-parameters {sorted(unknown)}")
+    d.update(kw)
+    ints = {"nesterov", "ns_steps", "lr_scale_mode", "ns_precision"}
+    return Hparams(**{k: (int(v) if k in ints else float(v)) for k, v in d.items()})
+
+
+@dataclass(frozen=True)
+class TableEntry:
+    offset: int
+    rows: int
+    cols: int
+    dtype: int = BF16
+    role: int = ROLE_AUTO
+
+
+class OwnerPlan:
+    """A lowered owner table (mfsdp_plan_t) and its step call."""
+
+    def __init__(self, entries: Sequence[TableEntry], param_bytes: int, hparams: Hparams):
+        lib = load()
+        arr = (Entry * max(1, len(entries)))()
+        for i, e in enumerate(entries):
+            arr[i] = Entry(e.offset, e.rows, e.cols, e.dtype, e.role)
+        handle = ctypes.c_void_p()
+        self.hparams = hparams
+        _check(lib.mfsdp_plan_create(arr, len(entries), param_bytes, ctypes.byref(hparams), ctypes.byref(handle)))
+        self._h = handle
+        self._lib = lib
+        self.n_entries = len(entries)
+
+    def _u64(self, fn) -> int:
+        v = ctypes.c_uint64()
+        _check(fn(self._h, ctypes.byref(v)))
+        return v.value
+
+    @property
+    def state_bytes(self) -> int:
+        return self._u64(self._lib.mfsdp_plan_state_bytes)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return self._u64(self._lib.mfsdp_plan_workspace_bytes)
+
+    @property
+    def ns_out_elems(self) -> int:
+        return self._u64(self._lib.mfsdp_plan_ns_out_elems)
+
+    def num_entries(self) -> int:
+        v = ctypes.c_int64()
+        _check(self._lib.mfsdp_plan_num_entries(self._h, ctypes.byref(v)))
+        return v.value
+
+    def entry_info(self, i: int) -> EntryInfo:
+        info = EntryInfo()
+        _check(self._lib.mfsdp_plan_entry_info(self._h, i, ctypes.byref(info)))
+        return info
+
+    def step(self, params: int, grads: int, state: int, workspace: int, workspace_bytes: int, step: int,
+             stream: int = 0, ns_out: int = 0, flags: int = 0) -> None:
+        args = StepArgs(params, grads, state, workspace, workspace_bytes, step, stream or None, ns_out or None, flags)
+        _check(self._lib.mfsdp_owner_step(self._h, ctypes.byref(args)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.mfsdp_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

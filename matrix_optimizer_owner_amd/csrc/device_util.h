@@ -1,0 +1,66 @@
+// device_util.h - small device helpers for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfsdp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Storage-type traits of the Newton-Schulz buffers: uint16_t holds bf16 bits.
+template <typename T> struct Store;
+template <> struct Store<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+    __device__ __forceinline__ static uint16_t cvt(float f) { return f32_to_bf16(f); }
+};
+template <> struct Store<float> {
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static float cvt(float f) { return f; }
+};
+
+// Parameter / gradient element access by runtime dtype (0 = fp32, 1 = bf16).
+__device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t i) {
+    return dtype == 1 ? bf16_to_f32(static_cast<const uint16_t*>(base)[i]) : static_cast<const float*>(base)[i];
+}
+__device__ __forceinline__ void store_elem(void* base, int dtype, int64_t i, float v) {
+    if (dtype == 1)
+        static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+    else
+        static_cast<float*>(base)[i] = v;
+}
+
+// Sum over a 64-lane wavefront (fixed butterfly order: deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Largest k in [0, n) with begin[k] <= x, for a non-decreasing prefix array.
+__device__ __forceinline__ int upper_index(const int32_t* begin, int n, int x) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (begin[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace mfsdp

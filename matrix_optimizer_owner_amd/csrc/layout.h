@@ -1,0 +1,85 @@
+// layout.h - device descriptor formats and tiling constants shared by the
+// host planner (plan.cpp, plain C++) and the HIP kernels.
+//
+// Workspace map (byte offsets, all 256-byte aligned):
+//   [desc]      descriptor blob written by the step from the plan:
+//                 MatDesc[n_mat], k1_begin[n_mat+1], Tile gram[], Tile poly[],
+//                 Tile upd[], TailDesc[n_tail], tail_begin[n_tail+1]
+//   [s]         float[n_mat]: 1/(||U||_F + eps) per Muon matrix
+//   [partials]  float[n_k1_blocks]: sum of u^2 over one 64x64 tile
+//   per matrix: X (mp x np), XT0 and XT1 (np x mp), A and B (mp x mp) in the
+//               Newton-Schulz storage type (bf16 or fp32), row-major.
+//
+// Orientation: every Muon matrix is handled as X (m x n, m <= n).  A tall
+// matrix (rows > cols) is stored transposed.  m and n are padded to
+// multiples of kPad with zeros; the zeros stay zero through every
+// Newton-Schulz iteration (rows and columns of zeros map to zeros), so the
+// contraction kernels need no bounds checks.  X is kept in both layouts: X
+// row-major feeds the Gram X X^T, X^T row-major (XT) feeds B X as the second
+// operand of a product whose operands are both contiguous along the
+// contraction index.
+#pragma once
+#include <stdint.h>
+
+namespace mfsdp {
+
+constexpr int kPad = 256;          // padding granule of m and n in the workspace
+constexpr int kTile = 128;         // output tile edge of the contraction kernels
+constexpr int kK1Tile = 64;        // tile edge of the momentum / transpose kernel
+constexpr int kTailChunk = 2048;   // elements per AdamW block
+constexpr uint64_t kAlign = 256;
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+
+struct MatDesc {
+    uint64_t param_off;    // bytes into params and grads
+    uint64_t mom_off;      // bytes into state (fp32 momentum, rows x cols)
+    uint64_t x_off;        // bytes into workspace: X  (mp x np)
+    uint64_t xt_off[2];    // bytes into workspace: XT ping-pong (np x mp)
+    uint64_t a_off;        // bytes into workspace: A  (mp x mp)
+    uint64_t b_off;        // bytes into workspace: B  (mp x mp)
+    uint64_t ns_out_off;   // element offset into ns_out (fp32, rows x cols)
+    int32_t rows, cols;    // shape as given
+    int32_t m, n;          // oriented, m <= n
+    int32_t mp, np;        // padded to kPad
+    int32_t transposed;    // rows > cols
+    int32_t dtype;         // param / grad storage type
+    float lr_scale;        // shape scale of the learning rate
+    int32_t k1_tiles_c;    // momentum-kernel tile columns (natural layout)
+};
+
+// One output tile of a grouped contraction: matrix index and tile coordinates
+// in units of kTile.
+struct Tile {
+    uint32_t mat;
+    uint16_t ti, tj;
+};
+
+struct TailDesc {
+    uint64_t param_off;    // bytes into params and grads
+    uint64_t m1_off;       // bytes into state (fp32)
+    uint64_t m2_off;       // bytes into state (fp32)
+    int64_t numel;
+    int32_t dtype;
+    int32_t pad_;
+};
+
+static_assert(sizeof(MatDesc) == 8 * 8 + 4 * 10, "MatDesc layout");
+static_assert(sizeof(Tile) == 8, "Tile layout");
+static_assert(sizeof(TailDesc) == 40, "TailDesc layout");
+
+// Byte offsets of the sections of the descriptor blob and of the fixed
+// workspace regions, plus element counts; filled by the planner.
+struct WorkspaceMap {
+    uint64_t desc_bytes;
+    uint64_t off_mat, off_k1_begin, off_gram, off_poly, off_upd, off_tail, off_tail_begin;
+    uint64_t off_s, off_partials;
+    uint64_t total_bytes;
+    int32_t n_mat, n_tail;
+    int32_t n_gram, n_poly, n_upd;
+    int32_t n_k1_blocks, n_tail_chunks;
+};
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace mfsdp

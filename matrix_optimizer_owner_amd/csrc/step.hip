@@ -1,0 +1,79 @@
+// step.hip - mfsdp_owner_step: enqueue one owner step on the caller's stream.
+//
+// Order on the stream: descriptor upload (unless resident), AdamW tail,
+// momentum/cast/norm partials, norm finalize, ns_steps x (Gram, polynomial,
+// update), the last update carrying the parameter write.  Nothing here
+// synchronises; the owner step of MatrixFSDP (arXiv 2607.05895, Abstract)
+// has no collective inside it, so the whole step is local to this stream.
+#include <cmath>
+#include <string>
+
+#include "kernels.h"
+#include "plan_internal.h"
+
+using namespace mfsdp;
+
+namespace {
+
+mfsdp_status hip_fail(hipError_t e, const char* what) {
+    return fail(MFSDP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args) {
+    clear_error();
+    if (!plan || !args) return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL plan or args");
+    const WorkspaceMap& map = plan->map;
+    const bool any = map.n_mat > 0 || map.n_tail > 0;
+    if (!any) return MFSDP_OK;  // nothing but empty shards
+    if (!args->params || !args->grads)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "params or grads is NULL");
+    if (!args->state && plan->state_bytes > 0) return fail(MFSDP_ERR_INVALID_ARGUMENT, "state is NULL");
+    if (!args->workspace) return fail(MFSDP_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(args->workspace) % kAlign != 0)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(args->params) % 16 != 0 || reinterpret_cast<uintptr_t>(args->grads) % 16 != 0 ||
+        (args->state && reinterpret_cast<uintptr_t>(args->state) % kAlign != 0))
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "params/grads must be 16-byte aligned and state 256-byte aligned");
+    if (args->workspace_bytes < map.total_bytes)
+        return fail(MFSDP_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace has " + std::to_string(args->workspace_bytes) + " bytes, plan needs " +
+                        std::to_string(map.total_bytes));
+    if (map.n_tail > 0 && args->step < 1)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "step must be >= 1 (AdamW bias correction is 1-based)");
+    if (args->ns_out && reinterpret_cast<uintptr_t>(args->ns_out) % 16 != 0)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_out must be 16-byte aligned");
+
+    hipStream_t stream = static_cast<hipStream_t>(args->stream);
+    StepBuffers b;
+    b.params = static_cast<uint8_t*>(args->params);
+    b.grads = static_cast<const uint8_t*>(args->grads);
+    b.state = static_cast<uint8_t*>(args->state);
+    b.ws = static_cast<uint8_t*>(args->workspace);
+    b.ns_out = args->ns_out;
+
+    hipError_t e;
+    if (!(args->flags & MFSDP_STEP_DESCRIPTORS_RESIDENT) && !plan->desc_blob.empty()) {
+        e = hipMemcpyAsync(b.ws, plan->desc_blob.data(), plan->desc_blob.size(), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "descriptor upload");
+    }
+    if (map.n_tail > 0) {
+        e = launch_adamw(map, plan->hp, args->step, b, stream);
+        if (e != hipSuccess) return hip_fail(e, "AdamW launch");
+    }
+    if (map.n_mat > 0) {
+        const int prec = plan->hp.ns_precision;
+        e = launch_momentum(prec, map, plan->hp, b, stream);
+        if (e != hipSuccess) return hip_fail(e, "momentum launch");
+        if (plan->hp.ns_steps == 0) {
+            e = launch_final_from_x(prec, map, plan->hp, b, stream);
+            if (e != hipSuccess) return hip_fail(e, "update launch");
+        }
+        for (int it = 1; it <= plan->hp.ns_steps; ++it) {
+            e = launch_ns_iteration(prec, map, plan->hp, it, b, stream);
+            if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
+        }
+    }
+    return MFSDP_OK;
+}
