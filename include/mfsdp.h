@@ -126,6 +126,13 @@ typedef struct mfsdp_step_args {
     float* ns_out;            /* NULL, or device fp32 [mfsdp_plan_ns_out_elems]: O per Muon entry,
                                  row-major in the entry's own shape, at entry_info.ns_out_offset */
     uint32_t flags;           /* MFSDP_STEP_* */
+    void** events;            /* NULL, or n_events hipEvent_t created by the caller: the step
+                                 records events[0] after the descriptor upload, events[1] after
+                                 the AdamW tail, events[2] after momentum + norm, and for
+                                 Newton-Schulz iteration k (1-based) events[3k], events[3k+1],
+                                 events[3k+2] after its Gram, polynomial and update launches.
+                                 Every event is recorded even when its phase is empty. */
+    uint32_t n_events;        /* must be >= mfsdp_plan_num_events when events != NULL */
 } mfsdp_step_args;
 
 /* Validate an owner table and lower it to a plan (host only; no HIP call).
@@ -148,6 +155,10 @@ mfsdp_status mfsdp_plan_workspace_bytes(mfsdp_plan_t plan, uint64_t* bytes);
 /* Number of fp32 elements of the optional ns_out export. */
 mfsdp_status mfsdp_plan_ns_out_elems(mfsdp_plan_t plan, uint64_t* elems);
 
+/* Number of phase-boundary events a step records when args->events is set
+ * (3 + 3*ns_steps). */
+mfsdp_status mfsdp_plan_num_events(mfsdp_plan_t plan, uint32_t* n);
+
 /* Number of table entries and the layout facts of entry i. */
 mfsdp_status mfsdp_plan_num_entries(mfsdp_plan_t plan, int64_t* n);
 mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsdp_entry_info* info);
@@ -158,7 +169,7 @@ mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsdp_entry_inf
  * stream at a time; two steps that share a workspace must not overlap.
  * Errors: INVALID_ARGUMENT (null plan or args, null buffer needed by the
  * table, step < 1 with an AdamW entry, misaligned workspace),
- * WORKSPACE_TOO_SMALL, HIP. */
+ * too few events), WORKSPACE_TOO_SMALL, HIP. */
 mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args);
 
 /* Free a plan.  NULL is accepted. */

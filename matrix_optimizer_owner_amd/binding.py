@@ -58,12 +58,13 @@ class EntryInfo(ctypes.Structure):
 class StepArgs(ctypes.Structure):
     _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("state", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64), ("step", ctypes.c_int64),
-                ("stream", ctypes.c_void_p), ("ns_out", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+                ("stream", ctypes.c_void_p), ("ns_out", ctypes.c_void_p), ("flags", ctypes.c_uint32),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_uint32)]
 
 
 EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
-    "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
+    "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
     "mfsdp_status_string", "mfsdp_last_error_message",
 )
 
@@ -85,6 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_plan_state_bytes.argtypes = [P, u64p]
     lib.mfsdp_plan_workspace_bytes.argtypes = [P, u64p]
     lib.mfsdp_plan_ns_out_elems.argtypes = [P, u64p]
+    lib.mfsdp_plan_num_events.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     lib.mfsdp_plan_num_entries.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.mfsdp_plan_entry_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(EntryInfo)]
     lib.mfsdp_owner_step.argtypes = [P, ctypes.POINTER(StepArgs)]
@@ -177,9 +179,16 @@ class OwnerPlan:
         _check(self._lib.mfsdp_plan_entry_info(self._h, i, ctypes.byref(info)))
         return info
 
+    def num_events(self) -> int:
+        v = ctypes.c_uint32()
+        _check(self._lib.mfsdp_plan_num_events(self._h, ctypes.byref(v)))
+        return v.value
+
     def step(self, params: int, grads: int, state: int, workspace: int, workspace_bytes: int, step: int,
-             stream: int = 0, ns_out: int = 0, flags: int = 0) -> None:
-        args = StepArgs(params, grads, state, workspace, workspace_bytes, step, stream or None, ns_out or None, flags)
+             stream: int = 0, ns_out: int = 0, flags: int = 0, events: Sequence[int] = ()) -> None:
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        args = StepArgs(params, grads, state, workspace, workspace_bytes, step, stream or None, ns_out or None, flags,
+                        ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None, len(events))
         _check(self._lib.mfsdp_owner_step(self._h, ctypes.byref(args)))
 
     def close(self) -> None:

@@ -29,9 +29,10 @@ hipError_t launch_final_from_x(int ns_precision, const WorkspaceMap& map, const 
 hipError_t launch_adamw(const WorkspaceMap& map, const mfsdp_hparams& hp, int64_t step,
                         const StepBuffers& b, hipStream_t stream);
 
-// One Newton-Schulz iteration (Gram, polynomial, update) over every matrix.
-// iter is 1-based; the last iteration applies the parameter update.
-hipError_t launch_ns_iteration(int ns_precision, const WorkspaceMap& map, const mfsdp_hparams& hp,
-                               int iter, const StepBuffers& b, hipStream_t stream);
+// One phase of Newton-Schulz iteration `iter` (1-based) over every matrix:
+// phase 0 Gram, 1 polynomial, 2 update (the last iteration's update applies
+// the parameter update).
+hipError_t launch_ns_phase(int ns_precision, const WorkspaceMap& map, const mfsdp_hparams& hp, int iter,
+                           int phase, const StepBuffers& b, hipStream_t stream);
 
 }  // namespace mfsdp

@@ -236,8 +236,8 @@ __global__ __launch_bounds__(256, 2) void k_ns_gemm(GemmArgs a) {
 }
 
 template <typename T>
-hipError_t launch_iter(const WorkspaceMap& map, const mfsdp_hparams& hp, int iter, const StepBuffers& b,
-                       hipStream_t stream) {
+hipError_t launch_phase(const WorkspaceMap& map, const mfsdp_hparams& hp, int iter, int phase,
+                        const StepBuffers& b, hipStream_t stream) {
     GemmArgs a;
     a.mats = reinterpret_cast<const MatDesc*>(b.ws + map.off_mat);
     a.ws = b.ws;
@@ -249,37 +249,32 @@ hipError_t launch_iter(const WorkspaceMap& map, const mfsdp_hparams& hp, int ite
     a.cc = hp.ns_c;
     a.lrwd = float(double(hp.lr) * double(hp.weight_decay));
     a.lr = hp.lr;
-    a.first = iter == 1;
+    a.first = iter == 1 && phase != 1;  // the polynomial sees an already normalised A
     a.xt_in = (iter - 1) & 1;
     a.xt_out = iter & 1;
     const dim3 blk(256);
-
-    a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_gram);
-    k_ns_gemm<T, kGram><<<dim3(map.n_gram), blk, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    a.first = 0;  // A is already normalised
-    a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_poly);
-    k_ns_gemm<T, kPoly><<<dim3(map.n_poly), blk, 0, stream>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    a.first = iter == 1;
-    a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_upd);
-    if (iter == hp.ns_steps)
-        k_ns_gemm<T, kFinal><<<dim3(map.n_upd), blk, 0, stream>>>(a);
-    else
-        k_ns_gemm<T, kUpdate><<<dim3(map.n_upd), blk, 0, stream>>>(a);
+    if (phase == 0) {
+        a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_gram);
+        k_ns_gemm<T, kGram><<<dim3(map.n_gram), blk, 0, stream>>>(a);
+    } else if (phase == 1) {
+        a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_poly);
+        k_ns_gemm<T, kPoly><<<dim3(map.n_poly), blk, 0, stream>>>(a);
+    } else {
+        a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_upd);
+        if (iter == hp.ns_steps)
+            k_ns_gemm<T, kFinal><<<dim3(map.n_upd), blk, 0, stream>>>(a);
+        else
+            k_ns_gemm<T, kUpdate><<<dim3(map.n_upd), blk, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ns_iteration(int ns_precision, const WorkspaceMap& map, const mfsdp_hparams& hp, int iter,
-                               const StepBuffers& b, hipStream_t stream) {
-    if (ns_precision == 1) return launch_iter<float>(map, hp, iter, b, stream);
-    return launch_iter<uint16_t>(map, hp, iter, b, stream);
+hipError_t launch_ns_phase(int ns_precision, const WorkspaceMap& map, const mfsdp_hparams& hp, int iter, int phase,
+                           const StepBuffers& b, hipStream_t stream) {
+    if (ns_precision == 1) return launch_phase<float>(map, hp, iter, phase, b, stream);
+    return launch_phase<uint16_t>(map, hp, iter, phase, b, stream);
 }
 
 }  // namespace mfsdp

@@ -333,6 +333,13 @@ extern "C" mfsdp_status mfsdp_plan_ns_out_elems(mfsdp_plan_t plan, uint64_t* ele
     return MFSDP_OK;
 }
 
+extern "C" mfsdp_status mfsdp_plan_num_events(mfsdp_plan_t plan, uint32_t* n) {
+    clear_error();
+    if (!plan || !n) return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL argument");
+    *n = uint32_t(3 + 3 * plan->hp.ns_steps);
+    return MFSDP_OK;
+}
+
 extern "C" mfsdp_status mfsdp_plan_num_entries(mfsdp_plan_t plan, int64_t* n) {
     clear_error();
     if (!plan || !n) return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL argument");

@@ -45,6 +45,10 @@ extern "C" mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_arg
     if (args->ns_out && reinterpret_cast<uintptr_t>(args->ns_out) % 16 != 0)
         return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_out must be 16-byte aligned");
 
+    const uint32_t n_events = uint32_t(3 + 3 * plan->hp.ns_steps);
+    if (args->events && args->n_events < n_events)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "events array needs " + std::to_string(n_events) + " entries");
+
     hipStream_t stream = static_cast<hipStream_t>(args->stream);
     StepBuffers b;
     b.params = static_cast<uint8_t*>(args->params);
@@ -54,25 +58,36 @@ extern "C" mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_arg
     b.ns_out = args->ns_out;
 
     hipError_t e;
+    auto mark = [&](uint32_t k) -> hipError_t {
+        return args->events ? hipEventRecord(static_cast<hipEvent_t>(args->events[k]), stream) : hipSuccess;
+    };
     if (!(args->flags & MFSDP_STEP_DESCRIPTORS_RESIDENT) && !plan->desc_blob.empty()) {
         e = hipMemcpyAsync(b.ws, plan->desc_blob.data(), plan->desc_blob.size(), hipMemcpyHostToDevice, stream);
         if (e != hipSuccess) return hip_fail(e, "descriptor upload");
     }
+    if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
     if (map.n_tail > 0) {
         e = launch_adamw(map, plan->hp, args->step, b, stream);
         if (e != hipSuccess) return hip_fail(e, "AdamW launch");
     }
+    if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event record");
+    const int prec = plan->hp.ns_precision;
     if (map.n_mat > 0) {
-        const int prec = plan->hp.ns_precision;
         e = launch_momentum(prec, map, plan->hp, b, stream);
         if (e != hipSuccess) return hip_fail(e, "momentum launch");
         if (plan->hp.ns_steps == 0) {
             e = launch_final_from_x(prec, map, plan->hp, b, stream);
             if (e != hipSuccess) return hip_fail(e, "update launch");
         }
-        for (int it = 1; it <= plan->hp.ns_steps; ++it) {
-            e = launch_ns_iteration(prec, map, plan->hp, it, b, stream);
-            if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
+    }
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
+    for (int it = 1; it <= plan->hp.ns_steps; ++it) {
+        for (int ph = 0; ph < 3; ++ph) {
+            if (map.n_mat > 0) {
+                e = launch_ns_phase(prec, map, plan->hp, it, ph, b, stream);
+                if (e != hipSuccess) return hip_fail(e, "Newton-Schulz launch");
+            }
+            if ((e = mark(uint32_t(3 * it + ph))) != hipSuccess) return hip_fail(e, "event record");
         }
     }
     return MFSDP_OK;
