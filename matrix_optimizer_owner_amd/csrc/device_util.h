@@ -8,15 +8,17 @@ namespace mfsdp {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byte granule
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// float -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet
+// NaN.  Branch-free (a select), so it does not diverge inside epilogues.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 // Storage-type traits of the Newton-Schulz buffers: uint16_t holds bf16 bits.

@@ -24,7 +24,9 @@
 namespace mfsdp {
 
 constexpr int kPad = 256;          // padding granule of m and n in the workspace
-constexpr int kTile = 128;         // output tile edge of the contraction kernels
+constexpr int kTileSmall = 128;    // output tile edges of the contraction kernels
+constexpr int kTileLarge = 256;
+constexpr int kLargeTileMin = 512; // a phase uses 256-tiles when it has at least this many
 constexpr int kK1Tile = 64;        // tile edge of the momentum / transpose kernel
 constexpr int kTailChunk = 2048;   // elements per AdamW block
 constexpr uint64_t kAlign = 256;
@@ -49,7 +51,7 @@ struct MatDesc {
 };
 
 // One output tile of a grouped contraction: matrix index and tile coordinates
-// in units of kTile.
+// in units of the phase's tile edge.
 struct Tile {
     uint32_t mat;
     uint16_t ti, tj;
@@ -78,6 +80,7 @@ struct WorkspaceMap {
     int32_t n_mat, n_tail;
     int32_t n_gram, n_poly, n_upd;
     int32_t n_k1_blocks, n_tail_chunks;
+    int32_t tile_gram, tile_poly, tile_upd;  // tile edge of each contraction phase
 };
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }

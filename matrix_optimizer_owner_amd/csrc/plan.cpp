@@ -9,6 +9,8 @@
 // non-owners hold empty shards).
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -27,7 +29,7 @@ void clear_error() { g_last_error.clear(); }
 
 namespace {
 
-constexpr int64_t kMaxDim = int64_t(1) << 22;  // uint16 tile indices at kTile=128 need < 2^23
+constexpr int64_t kMaxDim = int64_t(1) << 22;  // uint16 tile indices at 128-tiles need < 2^23
 
 int elem_bytes(int32_t dtype) { return dtype == kBF16 ? 2 : 4; }
 
@@ -57,18 +59,38 @@ float shape_scale(int64_t rows, int64_t cols, int mode) {
     return float(0.2 * std::sqrt(double(std::max(rows, cols))));
 }
 
-// Tiles of one matrix for one phase, in an order that keeps consecutive tiles
-// on shared operand panels: groups of 8 tile rows, columns inside a group.
+// Tiles of one matrix for one phase in 2D chunks of kChunkRows x kChunkCols
+// tiles (upper-triangle tiles only for the symmetric phases).  A chunk is what
+// one XCD works on at a time, so the operand panels it touches are few and
+// shared through that XCD's L2.
+constexpr int kChunkRows = 8, kChunkCols = 4, kChunk = kChunkRows * kChunkCols, kXcds = 8;
+
 void emit_tiles(std::vector<Tile>& out, uint32_t mat, int tm, int tn, bool upper) {
-    const int group = 8;
-    for (int g0 = 0; g0 < tm; g0 += group) {
-        const int g1 = std::min(tm, g0 + group);
-        for (int tj = 0; tj < tn; ++tj)
-            for (int ti = g0; ti < g1; ++ti) {
-                if (upper && ti > tj) continue;
-                out.push_back(Tile{mat, uint16_t(ti), uint16_t(tj)});
-            }
+    for (int r0 = 0; r0 < tm; r0 += kChunkRows)
+        for (int c0 = upper ? (r0 / kChunkCols) * kChunkCols : 0; c0 < tn; c0 += kChunkCols)
+            for (int tj = c0; tj < std::min(tn, c0 + kChunkCols); ++tj)
+                for (int ti = r0; ti < std::min(tm, r0 + kChunkRows); ++ti) {
+                    if (upper && ti > tj) continue;
+                    out.push_back(Tile{mat, uint16_t(ti), uint16_t(tj)});
+                }
+}
+
+// Reorder a logical tile list (cost-sorted, chunked) into launch order.
+// Workgroup w of a launch runs on XCD w % 8; give each XCD whole consecutive
+// chunks of kChunk logical tiles: in every round of 8 chunks, chunk k goes to
+// XCD k, its tiles at launch indices (round*kChunk + t)*8 + k.  A trailing
+// partial round keeps the logical order.
+std::vector<Tile> xcd_order(const std::vector<Tile>& logical) {
+    const size_t n = logical.size();
+    const size_t per_round = size_t(kChunk) * kXcds;
+    const size_t full = n / per_round * per_round;
+    std::vector<Tile> out(n);
+    for (size_t i = 0; i < full; ++i) {
+        const size_t round = i / per_round, k = (i % per_round) / kChunk, t = i % kChunk;
+        out[(round * kChunk + t) * kXcds + k] = logical[i];
     }
+    for (size_t i = full; i < n; ++i) out[i] = logical[i];
+    return out;
 }
 
 }  // namespace
@@ -229,13 +251,41 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             std::stable_sort(o.begin(), o.end(), [&](int x, int y) { return cost(x) > cost(y); });
             return o;
         };
+        // tile edge per phase: 256 when the phase has enough 256-tiles to fill
+        // the chip several times over, else 128
+        auto count = [&](bool upper, bool full_n, int t) {
+            int64_t c = 0;
+            for (const MatDesc& d : mats) {
+                const int64_t tm = d.mp / t, tn = full_n ? d.np / t : tm;
+                c += upper ? tm * (tm + 1) / 2 : tm * tn;
+            }
+            return c;
+        };
+        // tuning override MFSDP_TILE: "E" for every phase or "G,P,U" per phase (E, G, P, U in {128, 256})
+        int forced[3] = {0, 0, 0};
+        if (const char* f = std::getenv("MFSDP_TILE")) {
+            int v[3] = {0, 0, 0};
+            const int got = std::sscanf(f, "%d,%d,%d", &v[0], &v[1], &v[2]);
+            for (int k = 0; k < 3; ++k) {
+                const int x = got == 3 ? v[k] : v[0];
+                if (x == kTileSmall || x == kTileLarge) forced[k] = x;
+            }
+        }
+        auto pick = [&](int phase, bool upper, bool full_n) {
+            if (forced[phase]) return forced[phase];
+            return count(upper, full_n, kTileLarge) >= kLargeTileMin ? kTileLarge : kTileSmall;
+        };
+        const int tg = pick(0, true, false), tp = pick(1, true, false), tu = pick(2, false, true);
         std::vector<Tile> gram, poly, upd;
         for (int k : by_cost([&](int x) { return int64_t(mats[size_t(x)].np); }))
-            emit_tiles(gram, uint32_t(k), mats[size_t(k)].mp / kTile, mats[size_t(k)].mp / kTile, true);
+            emit_tiles(gram, uint32_t(k), mats[size_t(k)].mp / tg, mats[size_t(k)].mp / tg, true);
         for (int k : by_cost([&](int x) { return int64_t(mats[size_t(x)].mp); }))
-            emit_tiles(poly, uint32_t(k), mats[size_t(k)].mp / kTile, mats[size_t(k)].mp / kTile, true);
+            emit_tiles(poly, uint32_t(k), mats[size_t(k)].mp / tp, mats[size_t(k)].mp / tp, true);
         for (int k : by_cost([&](int x) { return int64_t(mats[size_t(x)].mp); }))
-            emit_tiles(upd, uint32_t(k), mats[size_t(k)].mp / kTile, mats[size_t(k)].np / kTile, false);
+            emit_tiles(upd, uint32_t(k), mats[size_t(k)].mp / tu, mats[size_t(k)].np / tu, false);
+        gram = xcd_order(gram);
+        poly = xcd_order(poly);
+        upd = xcd_order(upd);
 
         std::vector<int32_t> k1_begin(1, 0);
         for (const MatDesc& d : mats) {
@@ -289,6 +339,9 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         w.n_upd = int32_t(upd.size());
         w.n_k1_blocks = k1_begin.back();
         w.n_tail_chunks = tail_begin.back();
+        w.tile_gram = tg;
+        w.tile_poly = tp;
+        w.tile_upd = tu;
 
         plan->desc_blob.assign(size_t(w.desc_bytes), 0);
         auto put = [&](uint64_t at, const void* src, size_t bytes) {
