@@ -50,12 +50,14 @@ struct GemmArgs {
 
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
+    static constexpr int kSteps = 1;  // MFMA instructions per call
     __device__ __forceinline__ static void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
     }
 };
 template <> struct Mfma<float> {
+    static constexpr int kSteps = 4;
     __device__ __forceinline__ static void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -63,7 +65,8 @@ template <> struct Mfma<float> {
     }
 };
 
-// Four consecutive elements of the storage type (one transposed-store run).
+// Four consecutive elements of the storage type (the 4 accumulator rows one
+// lane holds, read or written along the transposed layout).
 template <typename T> struct Vec4;
 template <> struct Vec4<uint16_t> {
     typedef uint2 raw;
@@ -90,14 +93,6 @@ template <> struct Vec4<float> {
     }
 };
 
-constexpr int kGran = 8;  // 16-byte granules per LDS row (128 bytes of contraction index)
-
-// Physical granule of logical granule g in LDS row `row`.  The row term is
-// distinct over any 8 consecutive rows and over the 8 rows of one parity
-// among 16 consecutive rows, so a 16-byte-per-lane fragment read of
-// consecutive rows is free of bank conflicts with 32 or with 64 banks.
-__device__ __forceinline__ int swz(int row, int g) { return g ^ ((row + (row >> 3)) & 7); }
-
 template <typename W> struct Param;
 template <> struct Param<uint16_t> {
     __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -108,19 +103,36 @@ template <> struct Param<float> {
     __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
 };
 
-// Last Newton-Schulz update fused with the parameter write:
-// O = (a X + B X) [* s on a first iteration], then W <- W - lr*wd*W -
-// lr*scale*O in W's own orientation and O optionally exported in fp32.
-// In two halves of the tile's rows: every lane writes its O values into an
-// LDS tile laid out in W's orientation, then the block walks that tile in W's
-// memory order with 4-element vectors (coalesced W loads and stores).  X comes
-// from its transposed copy XT, whose 4 consecutive elements are the 4 rows a
-// lane holds.
+constexpr int kGran = 8;  // 16-byte granules per LDS row (128 bytes of contraction index)
+
+// Physical granule of logical granule g in LDS row `row` (128-byte rows):
+// g ^ ((row / 2) % 8).  Among the alternatives measured with the
+// SQ_LDS_BANK_CONFLICT counter on gfx950 (row % 8, (row + row/8) % 8,
+// (row/4) % 8, none, ...), this one gives zero bank conflicts for the
+// 16-byte-per-lane fragment reads of 32 consecutive rows.
+__device__ __forceinline__ int swz(int row, int g) { return g ^ ((row >> 1) & 7); }
+
+// Block shape: BT x BT output tile, NW wave64s in a 2 x (NW/2) grid; a wave
+// owns a (BT/2) x (2*BT/NW) block of MFMA 32x32 tiles.
+template <int BT, int NW>
+struct Shape {
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int WC = NW / 2;            // wave columns
+    static constexpr int WTM = BT / 2;           // wave tile rows
+    static constexpr int WTN = BT / WC;          // wave tile columns
+    static constexpr int MM = WTM / 32;          // MFMA tiles per wave along rows
+    static constexpr int MN = WTN / 32;          // MFMA tiles per wave along columns
+    static constexpr int LP = BT / (8 * NW);     // direct-to-LDS loads per wave, operand and stage
+};
+
+// LDS tile of the final update (one half of the tile's rows at a time), in
+// W's orientation: [BT/2][BT+4] floats when W is not transposed, else
+// [BT][BT/2+4].
 template <int BT>
 struct FinalLds {
-    static constexpr int HR = BT / 2;          // tile rows per half
-    static constexpr int PN = BT + 4;          // row pitch (floats), W not transposed: [HR][PN]
-    static constexpr int PT = HR + 4;          // row pitch (floats), W transposed:     [BT][PT]
+    static constexpr int HR = BT / 2;
+    static constexpr int PN = BT + 4;
+    static constexpr int PT = HR + 4;
     static constexpr int FLOATS = HR * PN > BT * PT ? HR * PN : BT * PT;
 };
 
@@ -162,12 +174,21 @@ __device__ __forceinline__ void w_update4(WT_* w, float* o_out, const float* o, 
     }
 }
 
-template <typename T, int MI, int WT, int BT>
-__device__ __forceinline__ void final_update(const f32x16_t (&acc)[MI][MI], const GemmArgs& a, const MatDesc& d,
-                                             int row0, int col0, int wm, int wn, int frow, int fhalf, float s1,
-                                             const T* XTin, float* olds) {
+// Last Newton-Schulz update fused with the parameter write:
+// O = (a X + B X) [* s on a first iteration], then W <- W - lr*wd*W -
+// lr*scale*O in W's own orientation and O optionally exported in fp32.
+// In two halves of the tile's rows: every lane writes its O values into an
+// LDS tile laid out in W's orientation, then the block walks that tile in W's
+// memory order with 4-element vectors (coalesced W loads and stores).  X comes
+// from its transposed copy XT, whose 4 consecutive elements are the 4 rows a
+// lane holds.
+template <typename T, int BT, int NW>
+__device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                             const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
+                                             int frow, int fhalf, float s1, const T* XTin, float* olds) {
+    using S = Shape<BT, NW>;
     using L = FinalLds<BT>;
-    constexpr int HW = WT / 2;  // rows of one wave's block per half
+    constexpr int HW = S::WTM / 2;  // rows of one wave's block per half
     const bool tr = d.transposed != 0;
     const float step = a.lr * d.lr_scale;
     const int mp = d.mp;
@@ -175,30 +196,29 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[MI][MI], cons
     const bool vec = (d.cols & 3) == 0;
     uint8_t* Wb = a.params + d.param_off;
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;
-    // W coordinates of a tile element (global tile row r, column c): (r, c), or (c, r) when transposed
     const int w_rows = d.rows, w_cols = d.cols;
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         // 1) O for this half into LDS, in W's orientation
 #pragma unroll
-        for (int mh = 0; mh < MI / 2; ++mh) {
-            const int mi = h * (MI / 2) + mh;
-            typename Vec4<T>::raw xv[MI][4];
+        for (int mh = 0; mh < S::MM / 2; ++mh) {
+            const int mi = h * (S::MM / 2) + mh;
+            typename Vec4<T>::raw xv[S::MN][4];
 #pragma unroll
-            for (int ni = 0; ni < MI; ++ni)
+            for (int ni = 0; ni < S::MN; ++ni)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int rb = row0 + wm * WT + mi * 32 + q * 8 + fhalf * 4;
-                    const int c = col0 + wn * WT + ni * 32 + frow;
+                    const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
+                    const int c = col0 + wn * S::WTN + ni * 32 + frow;
                     xv[ni][q] = Vec4<T>::load(XTin + int64_t(c) * mp + rb);
                 }
 #pragma unroll
-            for (int ni = 0; ni < MI; ++ni)
+            for (int ni = 0; ni < S::MN; ++ni)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int lr = wm * HW + mh * 32 + q * 8 + fhalf * 4;  // local row of the first of 4
-                    const int lc = wn * WT + ni * 32 + frow;                 // local column
+                    const int lc = wn * S::WTN + ni * 32 + frow;           // local column
                     float o[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -214,27 +234,26 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[MI][MI], cons
         __syncthreads();
         // 2) walk the half tile in W's memory order, 4 elements per step
         constexpr int CHUNKS = L::HR * BT / 4;
-#pragma unroll 4
-        for (int k = threadIdx.x; k < CHUNKS; k += 256) {
-            int lr, lc;  // local row (of the half) and local column of the chunk's first element
+#pragma unroll 2
+        for (int k = threadIdx.x; k < CHUNKS; k += S::kThreads) {
             float o[4];
             int64_t widx;
             int n_ok;
             if (tr) {
-                lc = k / (L::HR / 4);
-                lr = (k % (L::HR / 4)) * 4;
+                const int lc = k / (L::HR / 4);
+                const int lr = (k % (L::HR / 4)) * 4;
                 const float4 v = *reinterpret_cast<const float4*>(olds + lc * L::PT + lr);
                 o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-                const int gr = row0 + (lr / HW) * WT + h * HW + lr % HW;  // tile row -> W column
-                const int gc = col0 + lc;                                 // tile column -> W row
+                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;  // tile row -> W column
+                const int gc = col0 + lc;                                     // tile column -> W row
                 widx = int64_t(gc) * ldw + gr;
                 n_ok = gc < w_rows ? min(4, w_cols - gr) : 0;
             } else {
-                lr = k / (BT / 4);
-                lc = (k % (BT / 4)) * 4;
+                const int lr = k / (BT / 4);
+                const int lc = (k % (BT / 4)) * 4;
                 const float4 v = *reinterpret_cast<const float4*>(olds + lr * L::PN + lc);
                 o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-                const int gr = row0 + (lr / HW) * WT + h * HW + lr % HW;
+                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;
                 const int gc = col0 + lc;
                 widx = int64_t(gr) * ldw + gc;
                 n_ok = gr < w_rows ? min(4, w_cols - gc) : 0;
@@ -251,13 +270,39 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[MI][MI], cons
     }
 }
 
-// C = P Q^T over one BT x BT output tile; 4 waves in a 2x2 grid, each wave
-// (BT/2) x (BT/2) as (BT/64) x (BT/64) MFMA 32x32 tiles.
-template <typename T, int PHASE, int BT>
-__global__ __launch_bounds__(256, BT == 256 ? 1 : 2) void k_ns_gemm(GemmArgs a) {
-    constexpr int MI = BT / 64;     // MFMA tiles per wave along rows and along columns
-    constexpr int LP = BT / 32;     // global-load passes per operand (32 rows per pass)
-    constexpr int WT = BT / 2;      // wave tile edge
+// Scheduling groups for one stage of the main loop (bf16): sub-step 0 issues
+// the next stage's direct-to-LDS loads and sub-step 1's fragment reads among
+// its MFMAs, sub-steps 1 and 2 the following fragment reads, sub-step 3 only
+// MFMAs.
+template <int NMF, int NDS, int NVM>
+__device__ __forceinline__ void stage_schedule() {
+    constexpr int mf = NMF / NDS, vm = NVM / NDS;
+    constexpr int mf_tail = NMF - mf * NDS, vm_tail = NVM - vm * NDS;
+#pragma unroll
+    for (int t = 0; t < NDS; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);  // MFMA
+        if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
+    if constexpr (vm_tail > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm_tail, 0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int t = 0; t < NDS; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+}
+
+// C = P Q^T over one BT x BT output tile, then the phase's epilogue.
+template <typename T, int PHASE, int BT, int NW>
+__global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
+    using S = Shape<BT, NW>;
+    constexpr int MM = S::MM, MN = S::MN, LP = S::LP;
     // main loop: [stage][operand P/Q][row][granule]; the final epilogue reuses
     // the same bytes (slightly more of them) for its O tile
     constexpr int kMainBytes = 2 * 2 * BT * kGran * 16;
@@ -290,64 +335,96 @@ __global__ __launch_bounds__(256, BT == 256 ? 1 : 2) void k_ns_gemm(GemmArgs a) 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = tid >> 3, lgran = tid & 7;  // global-load assignment: 32 rows x 8 granules per pass
+    const int wm = wave / S::WC, wn = wave % S::WC;
+    const int frow = lane & 31;   // fragment row inside a 32-row MFMA tile
+    const int fhalf = lane >> 5;  // which 16-byte granule of a granule pair
 
-    const uint8_t* pbase = reinterpret_cast<const uint8_t*>(P + int64_t(row0 + lrow) * ldp) + lgran * 16;
-    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(Q + int64_t(col0 + lrow) * ldq) + lgran * 16;
-    const int64_t pstride = int64_t(32) * ldp * int64_t(sizeof(T));
-    const int64_t qstride = int64_t(32) * ldq * int64_t(sizeof(T));
-
-    u32x4_t rp[LP], rq[LP];
-    f32x16_t acc[MI][MI];
+    f32x16_t acc[MM][MN];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MM; ++i)
 #pragma unroll
-        for (int j = 0; j < MI; ++j)
+        for (int j = 0; j < MN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    // Operand tiles reach LDS by direct global->LDS loads (16 bytes per lane):
+    // one wave instruction fills 1 KB = 8 LDS rows, lane l landing at byte
+    // 16*l, i.e. row l/8, physical granule l%8.  The swizzle is applied on the
+    // global side: the lane fetches the logical granule stored there.  Wave w
+    // fills row groups i*NW + w, i = 0 .. LP-1, of each operand.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int lr8 = lane >> 3, lq = lane & 7;
+    const int64_t ldpb = int64_t(ldp) * int64_t(sizeof(T));
+    const int64_t ldqb = int64_t(ldq) * int64_t(sizeof(T));
+    const uint8_t* pl = reinterpret_cast<const uint8_t*>(P) + (int64_t(row0) + wave_u * 8 + lr8) * ldpb;
+    const uint8_t* ql = reinterpret_cast<const uint8_t*>(Q) + (int64_t(col0) + wave_u * 8 + lr8) * ldqb;
+    auto issue = [&](int kt, int st) {
+        const int64_t koff = int64_t(kt) * 128;
+#pragma unroll
+        for (int i = 0; i < LP; ++i) {
+            const int row = (i * NW + wave_u) * 8 + lr8;
+            const int64_t off = koff + swz(row, lq) * 16;
+            __builtin_amdgcn_global_load_lds(pl + int64_t(i) * NW * 8 * ldpb + off,
+                                             (__attribute__((address_space(3))) void*)&lds[st][0][(i * NW + wave_u) * 8][0],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ql + int64_t(i) * NW * 8 * ldqb + off,
+                                             (__attribute__((address_space(3))) void*)&lds[st][1][(i * NW + wave_u) * 8][0],
+                                             16, 0, 0);
+        }
+    };
+
     const int KT = K * int(sizeof(T)) / 128;  // stages of 128 bytes along the contraction index
-#define MFSDP_GLOAD(kt)                                                                        \
-    _Pragma("unroll") for (int i = 0; i < LP; ++i) {                                           \
-        rp[i] = *reinterpret_cast<const u32x4_t*>(pbase + i * pstride + int64_t(kt) * 128);   \
-        rq[i] = *reinterpret_cast<const u32x4_t*>(qbase + i * qstride + int64_t(kt) * 128);   \
-    }
-#define MFSDP_LSTORE(st)                                                                       \
-    _Pragma("unroll") for (int i = 0; i < LP; ++i) {                                           \
-        const int r = lrow + 32 * i;                                                           \
-        lds[st][0][r][swz(r, lgran)] = rp[i];                                                  \
-        lds[st][1][r][swz(r, lgran)] = rq[i];                                                  \
-    }
-    MFSDP_GLOAD(0)
-    MFSDP_LSTORE(0)
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int frow = lane & 31;   // fragment row inside a 32-row MFMA tile
-    const int fhalf = lane >> 5;  // which 16-byte granule of a granule pair
+    // Per stage: 4 contraction sub-steps (16 bf16 each) of MM x MN MFMA steps,
+    // fragments double-buffered across sub-steps.  Software pipeline across
+    // stages: the MFMAs of a stage's last sub-step (operands already in
+    // registers) are issued after the stage barrier, so they cover the LDS
+    // latency of the next stage's first fragments.  The loop body has no
+    // branch: the first deferred group multiplies zero fragments, and the last
+    // stage's look-ahead load and read hit the idle buffer.
+    auto frags = [&](int s, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
+#pragma unroll
+        for (int i = 0; i < MM; ++i) {
+            const int ra = wm * S::WTM + i * 32 + frow;
+            af[i] = lds[s][0][ra][swz(ra, 2 * kk + fhalf)];
+        }
+#pragma unroll
+        for (int j = 0; j < MN; ++j) {
+            const int rb = wn * S::WTN + j * 32 + frow;
+            bf[j] = lds[s][1][rb][swz(rb, 2 * kk + fhalf)];
+        }
+    };
+    auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+#pragma unroll
+            for (int j = 0; j < MN; ++j) Mfma<T>::step(acc[i][j], af[i], bf[j]);
+    };
+    u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
+#pragma unroll
+    for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < MN; ++j) fb1[j] = u32x4_t{0u, 0u, 0u, 0u};
+    frags(0, 0, fa0, fb0);
     for (int kt = 0; kt < KT; ++kt) {
         const int s = kt & 1;
-        if (kt + 1 < KT) { MFSDP_GLOAD(kt + 1) }
-#pragma unroll
-        for (int kk = 0; kk < kGran / 2; ++kk) {
-            u32x4_t af[MI], bf[MI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int ra = wm * WT + i * 32 + frow;
-                const int rb = wn * WT + i * 32 + frow;
-                af[i] = lds[s][0][ra][swz(ra, 2 * kk + fhalf)];
-                bf[i] = lds[s][1][rb][swz(rb, 2 * kk + fhalf)];
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < MI; ++j) Mfma<T>::step(acc[i][j], af[i], bf[j]);
-        }
-        if (kt + 1 < KT) { MFSDP_LSTORE(s ^ 1) }
+        issue(kt + 1 < KT ? kt + 1 : kt, s ^ 1);
+        mfmas(fa1, fb1);          // sub-step 3 of the previous stage (zeros on the first)
+        frags(s, 1, fa1, fb1);
+        mfmas(fa0, fb0);          // sub-step 0
+        frags(s, 2, fa0, fb0);
+        mfmas(fa1, fb1);          // sub-step 1
+        frags(s, 3, fa1, fb1);
+        mfmas(fa0, fb0);          // sub-step 2
+        if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, MM + MN, 2 * LP>();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        frags(s ^ 1, 0, fa0, fb0);  // next stage's first fragments
     }
-#undef MFSDP_GLOAD
-#undef MFSDP_LSTORE
+    mfmas(fa1, fb1);  // sub-step 3 of the last stage
 
     // ---- epilogue ----
     // Accumulator element e of the 32x32 MFMA tile (mi, ni) holds
@@ -372,64 +449,73 @@ __global__ __launch_bounds__(256, BT == 256 ? 1 : 2) void k_ns_gemm(GemmArgs a) 
     // issued one MFMA row block ahead.
     const T* Etr = PHASE == kPoly ? reinterpret_cast<const T*>(a.ws + d.a_off) : Q;
 
-    if (PHASE == kFinal) {
-        final_update<T, MI, WT, BT>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, Etr,
-                                    reinterpret_cast<float*>(lds_raw));
+    if constexpr (PHASE == kFinal) {
+        final_update<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, Etr,
+                                reinterpret_cast<float*>(lds_raw));
         return;
-    }
-
-    typename Vec4<T>::raw ev[2][MI][4];
-    if (PHASE != kGram) {
+    } else {
+        typename Vec4<T>::raw ev[2][MN][4];
+        if (PHASE != kGram) {
 #pragma unroll
-        for (int ni = 0; ni < MI; ++ni)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = col0 + wn * WT + ni * 32 + frow;
-                ev[0][ni][q] = Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * WT + q * 8 + fhalf * 4);
-            }
-    }
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        if (PHASE != kGram && mi + 1 < MI) {
-#pragma unroll
-            for (int ni = 0; ni < MI; ++ni)
+            for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c = col0 + wn * WT + ni * 32 + frow;
-                    ev[(mi + 1) & 1][ni][q] =
-                        Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * WT + (mi + 1) * 32 + q * 8 + fhalf * 4);
+                    const int c = col0 + wn * S::WTN + ni * 32 + frow;
+                    ev[0][ni][q] = Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * S::WTM + q * 8 + fhalf * 4);
                 }
         }
 #pragma unroll
-        for (int ni = 0; ni < MI; ++ni)
+        for (int mi = 0; mi < MM; ++mi) {
+            if (PHASE != kGram && mi + 1 < MM) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = row0 + wm * WT + mi * 32 + q * 8 + fhalf * 4;  // first of 4 rows
-                const int c = col0 + wn * WT + ni * 32 + frow;
-                float v[4];
+                for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = acc[mi][ni][q * 4 + e];
-                    if (PHASE == kGram)
-                        v[e] = x * (s1 * s1);
-                    else if (PHASE == kPoly)
-                        v[e] = a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * x;
-                    else
-                        v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + x) * s1;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[int64_t(rb + e) * ldo + c] = Store<T>::cvt(v[e]);
-                if (PHASE == kUpdate || !diag) Vec4<T>::store(outT + int64_t(c) * mp + rb, v[0], v[1], v[2], v[3]);
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = col0 + wn * S::WTN + ni * 32 + frow;
+                        ev[(mi + 1) & 1][ni][q] = Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * S::WTM +
+                                                                (mi + 1) * 32 + q * 8 + fhalf * 4);
+                    }
             }
+#pragma unroll
+            for (int ni = 0; ni < MN; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;  // first of 4 rows
+                    const int c = col0 + wn * S::WTN + ni * 32 + frow;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = acc[mi][ni][q * 4 + e];
+                        if (PHASE == kGram)
+                            v[e] = x * (s1 * s1);
+                        else if (PHASE == kPoly)
+                            v[e] = a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * x;
+                        else
+                            v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + x) * s1;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[int64_t(rb + e) * ldo + c] = Store<T>::cvt(v[e]);
+                    if (PHASE == kUpdate || !diag)
+                        Vec4<T>::store(outT + int64_t(c) * mp + rb, v[0], v[1], v[2], v[3]);
+                }
+        }
     }
 }
 
+// Wave count of the 256-tile kernels (4: one wave per SIMD with 128x128 each;
+// 8: two per SIMD with 128x64 each).
+#ifndef MFSDP_WAVES_256
+#define MFSDP_WAVES_256 8
+#endif
+
 template <typename T, int PHASE>
 void launch_tiles(const GemmArgs& a, int n_tiles, int tile, hipStream_t stream) {
-    if (tile == 256)
-        k_ns_gemm<T, PHASE, 256><<<dim3(n_tiles), dim3(256), 0, stream>>>(a);
-    else
-        k_ns_gemm<T, PHASE, 128><<<dim3(n_tiles), dim3(256), 0, stream>>>(a);
+    if (tile == 256) {
+        constexpr int NW = MFSDP_WAVES_256;
+        k_ns_gemm<T, PHASE, 256, NW><<<dim3(n_tiles), dim3(64 * NW), 0, stream>>>(a);
+    } else {
+        k_ns_gemm<T, PHASE, 128, 4><<<dim3(n_tiles), dim3(256), 0, stream>>>(a);
+    }
 }
 
 template <typename T>
