@@ -46,6 +46,7 @@ struct GemmArgs {
     float lr;
     int first;          // first iteration: scale by s (Gram: s^2)
     int xt_in, xt_out;  // XT ping-pong buffers read / written by the update
+    int n_tiles;        // tiles in the list; a block walks tiles blockIdx.x + k*gridDim.x
 };
 
 template <typename T> struct Mfma;
@@ -102,6 +103,32 @@ template <> struct Param<float> {
     __device__ __forceinline__ static float load(const float* p) { return *p; }
     __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
 };
+
+// 4x4 transpose inside each quad of lanes (lanes 4g..4g+3): on entry lane
+// 4g+j holds v[i] = element (row i, column j) of a 4x4 block; on exit it
+// holds v[i] = element (row j, column i).  Three DPP quad permutations (xor
+// 1, 2, 3); no LDS.  Turns the MFMA layout (4 consecutive rows per lane) into
+// 4 consecutive columns per lane for row-major stores.
+template <int CTRL>
+__device__ __forceinline__ float quad_xor(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int j) {
+    // round t: send v[j ^ t] to lane j ^ t; receive the partner's v[j], which is
+    // the output element at index j ^ t
+    float out[4];
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];  // t = 0 keeps v[j] at index j
+    const float s1 = v[j ^ 1], s2 = v[j ^ 2], s3 = v[j ^ 3];
+    const float r1 = quad_xor<0xB1>(s1);  // quad_perm [1,0,3,2]
+    const float r2 = quad_xor<0x4E>(s2);  // quad_perm [2,3,0,1]
+    const float r3 = quad_xor<0x1B>(s3);  // quad_perm [3,2,1,0]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = i ^ j;  // which round delivers output index i
+        out[i] = t == 0 ? v[i] : (t == 1 ? r1 : (t == 2 ? r2 : r3));
+    }
+    v[0] = out[0]; v[1] = out[1]; v[2] = out[2]; v[3] = out[3];
+}
 
 constexpr int kGran = 8;  // 16-byte granules per LDS row (128 bytes of contraction index)
 
@@ -298,19 +325,23 @@ __device__ __forceinline__ void stage_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
 }
 
-// C = P Q^T over one BT x BT output tile, then the phase's epilogue.
-template <typename T, int PHASE, int BT, int NW>
-__global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
-    using S = Shape<BT, NW>;
-    constexpr int MM = S::MM, MN = S::MN, LP = S::LP;
+template <int PHASE, int BT>
+struct LdsBytes {
     // main loop: [stage][operand P/Q][row][granule]; the final epilogue reuses
     // the same bytes (slightly more of them) for its O tile
-    constexpr int kMainBytes = 2 * 2 * BT * kGran * 16;
-    constexpr int kFinalBytes = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kMainBytes > kFinalBytes ? kMainBytes : kFinalBytes];
+    static constexpr int main_loop = 2 * 2 * BT * kGran * 16;
+    static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
+    static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
+};
+
+// C = P Q^T over one BT x BT output tile, then the phase's epilogue.
+template <typename T, int PHASE, int BT, int NW>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uint8_t* lds_raw) {
+    using S = Shape<BT, NW>;
+    constexpr int MM = S::MM, MN = S::MN, LP = S::LP;
     auto& lds = *reinterpret_cast<u32x4_t(*)[2][2][BT][kGran]>(lds_raw);
 
-    const Tile tile = a.tiles[blockIdx.x];
+    const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
     const int mp = d.mp, np = d.np;
     const int row0 = int(tile.ti) * BT, col0 = int(tile.tj) * BT;
@@ -493,12 +524,29 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
                         else
                             v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + x) * s1;
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) out[int64_t(rb + e) * ldo + c] = Store<T>::cvt(v[e]);
+                    // transposed store: the 4 rows of this lane are consecutive in outT
                     if (PHASE == kUpdate || !diag)
                         Vec4<T>::store(outT + int64_t(c) * mp + rb, v[0], v[1], v[2], v[3]);
+                    // row-major store: after a quad transpose lane 4g+j holds row rb+j,
+                    // columns 4g..4g+3 of this 32-column block
+                    const int j = frow & 3;
+                    quad_transpose(v, j);
+                    Vec4<T>::store(out + int64_t(rb + j) * ldo + (c - j), v[0], v[1], v[2], v[3]);
                 }
         }
+    }
+}
+
+// One block per tile: the hardware dispatcher then hands the cost-sorted
+// tile list to CUs as they free up (greedy longest-first).  A grid smaller
+// than the list would make each block walk tiles with a fixed stride; that
+// static split measured slower than dispatch on the Llama-3-8B share.
+template <typename T, int PHASE, int BT, int NW>
+__global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<PHASE, BT>::value];
+    for (int t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
+        gemm_tile<T, PHASE, BT, NW>(a, t, lds_raw);
+        __syncthreads();  // LDS free before the next tile's first loads
     }
 }
 
@@ -509,12 +557,14 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
 #endif
 
 template <typename T, int PHASE>
-void launch_tiles(const GemmArgs& a, int n_tiles, int tile, hipStream_t stream) {
+void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
+    a.n_tiles = n_tiles;
+    const int grid = n_tiles;
     if (tile == 256) {
         constexpr int NW = MFSDP_WAVES_256;
-        k_ns_gemm<T, PHASE, 256, NW><<<dim3(n_tiles), dim3(64 * NW), 0, stream>>>(a);
+        k_ns_gemm<T, PHASE, 256, NW><<<dim3(grid), dim3(64 * NW), 0, stream>>>(a);
     } else {
-        k_ns_gemm<T, PHASE, 128, 4><<<dim3(n_tiles), dim3(256), 0, stream>>>(a);
+        k_ns_gemm<T, PHASE, 128, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
     }
 }
 
