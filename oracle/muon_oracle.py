@@ -31,8 +31,8 @@ library receives, widened to fp64.  Matrix products use numpy's ``@``
 (BLAS DGEMM) as a library primitive; nothing is blocked, fused or reordered.
 
 Parity pins (tests/test_oracle_pins.py): Newton-Schulz against the SVD
-closed form U p^5(S) V^T, unchanged singular vectors, the output-band
-invariant, transpose symmetry (direct large-Gram evaluation), exact special
+closed form U p^5(S) V^T (the matrix form and the vector-applied form),
+unchanged singular vectors, the output-band invariant, transpose symmetry (direct large-Gram evaluation), exact special
 cases (zero, rank-1, [I 0]), scale invariance, momentum closed forms, AdamW
 step-1 and constant-gradient closed forms, and bf16 rounding against an
 exhaustive enumeration.  The learning-rate shape-scale convention and the
@@ -110,6 +110,46 @@ def newton_schulz(x: np.ndarray, steps: int, a: float, b: float, c: float) -> np
     return xw.T.copy() if tall else xw
 
 
+def newton_schulz_apply(x: np.ndarray, v: np.ndarray, steps: int, a: float, b: float, c: float) -> np.ndarray:
+    """NS_steps(X) @ V for a block of vectors V, without forming any matrix
+    product of X with itself: the same iteration, applied to vectors.
+
+    With X_0 = X (wide orientation) and X_k = a X_{k-1} + B_{k-1} X_{k-1},
+    B = b A + c A A, A = X_{k-1} X_{k-1}^T:
+        X_k y   = a z + b A z + c A (A z),   z = X_{k-1} y
+        X_k^T w = X_{k-1}^T (a w + b A w + c A (A w))   (B is symmetric)
+    and A z = X_{k-1} (X_{k-1}^T z).  The cost is about 5^k products of X_0
+    with a vector block, so this is for few steps on large matrices.  A tall
+    X is handled through its transpose, as in newton_schulz.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    tall = x.shape[0] > x.shape[1]
+    xw = x.T if tall else x
+
+    def fwd(k, y):  # X_k y  (wide: m x n times n-vectors)
+        if k == 0:
+            return xw @ y
+        z = fwd(k - 1, y)
+        return _poly(k - 1, z)
+
+    def bwd(k, w):  # X_k^T w
+        if k == 0:
+            return xw.T @ w
+        return bwd(k - 1, _poly(k - 1, w))
+
+    def _gram(k, z):  # A_k z = X_k (X_k^T z)
+        return fwd(k, bwd(k, z))
+
+    def _poly(k, z):  # (a I + b A_k + c A_k A_k) z
+        az = _gram(k, z)
+        return a * z + b * az + c * _gram(k, az)
+
+    if tall:  # X = X_w^T and NS(X) = NS(X_w)^T, so NS(X) V = NS(X_w)^T V
+        return bwd(steps, v)
+    return fwd(steps, v)
+
+
 def frobenius_normalise(u: np.ndarray, eps: float) -> np.ndarray:
     """X = U / (||U||_F + eps): the Newton-Schulz input."""
     u = np.asarray(u, dtype=np.float64)
@@ -134,6 +174,24 @@ def lr_shape_scale(rows: int, cols: int, mode: int) -> float:
 # so the update equals full-matrix Muon)
 # ---------------------------------------------------------------------------
 
+def momentum_step(m, g, hp: Hparams):
+    """Momentum smoothing: m <- beta m + g; the Newton-Schulz input is
+    u = g + beta m (Nesterov) or u = m.  Returns (m_new, u)."""
+    m = np.asarray(m, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = hp.momentum
+    m_new = beta * m + g
+    u = g + beta * m_new if hp.nesterov else m_new
+    return m_new, u
+
+
+def apply_update(w, o, rows: int, cols: int, hp: Hparams):
+    """W <- W (1 - lr wd) - lr * scale * O (decoupled weight decay)."""
+    w = np.asarray(w, dtype=np.float64)
+    scale = lr_shape_scale(rows, cols, hp.lr_scale_mode)
+    return w * (1.0 - hp.lr * hp.weight_decay) - hp.lr * scale * np.asarray(o, dtype=np.float64)
+
+
 def muon_matrix_step(w, g, m, hp: Hparams):
     """One Muon step for one whole matrix, all fp64.
 
@@ -141,16 +199,11 @@ def muon_matrix_step(w, g, m, hp: Hparams):
     matrix's own orientation.
     """
     w = np.asarray(w, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    m = np.asarray(m, dtype=np.float64)
     rows, cols = w.shape
-    beta = hp.momentum
-    m_new = beta * m + g
-    u = g + beta * m_new if hp.nesterov else m_new
+    m_new, u = momentum_step(m, g, hp)
     x = frobenius_normalise(u, hp.ns_eps)
     o = newton_schulz(x, hp.ns_steps, hp.ns_a, hp.ns_b, hp.ns_c)
-    scale = lr_shape_scale(rows, cols, hp.lr_scale_mode)
-    w_new = w * (1.0 - hp.lr * hp.weight_decay) - hp.lr * scale * o
+    w_new = apply_update(w, o, rows, cols, hp)
     return w_new, m_new, o
 
 

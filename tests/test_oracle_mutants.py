@@ -22,6 +22,8 @@ MUTANTS = {
     "no_normalisation": ("return u / (math.sqrt(float(np.sum(u * u))) + eps)", "return u"),
     "eps_inside_sqrt": ("math.sqrt(float(np.sum(u * u))) + eps", "math.sqrt(float(np.sum(u * u)) + eps)"),
     "nesterov_uses_old_momentum": ("u = g + beta * m_new if", "u = g + beta * m if"),
+    "apply_drops_cubic": ("return a * z + b * az + c * _gram(k, az)", "return a * z + c * _gram(k, az)"),
+    "apply_transpose_side": ("return bwd(k - 1, _poly(k - 1, w))", "return bwd(k - 1, w)"),
     "ema_momentum": ("m_new = beta * m + g", "m_new = beta * m + (1.0 - beta) * g"),
     "decay_not_lr_scaled": ("w * (1.0 - hp.lr * hp.weight_decay)", "w * (1.0 - hp.weight_decay)"),
     "shape_scale_inverted": ("max(1.0, rows / cols)", "max(1.0, cols / rows)"),

@@ -45,6 +45,19 @@ def test_ns_matches_svd_closed_form(shape, steps):
     assert rel <= 1e-12, rel
 
 
+@pytest.mark.parametrize("shape", [(6, 9), (9, 6), (16, 40), (33, 20)])
+@pytest.mark.parametrize("steps", [0, 1, 2, 3])
+def test_ns_apply_matches_svd_closed_form(shape, steps):
+    """The vector-applied iteration gives U p^k(S) V^T @ V for a block V."""
+    x = rand(shape, 3 + shape[1])
+    x = x / np.linalg.norm(x)
+    v = rand((shape[1], 3), 99)
+    u, s, vt = np.linalg.svd(x, full_matrices=False)
+    want = ((u * p5(s, steps)) @ vt) @ v
+    got = orc.newton_schulz_apply(x, v, steps, A, B, C)
+    assert np.linalg.norm(got - want) <= 1e-12 * np.linalg.norm(want)
+
+
 def test_ns_singular_vectors_unchanged():
     x = rand((24, 40), 3)
     x = x / np.linalg.norm(x)
