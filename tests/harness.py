@@ -100,6 +100,34 @@ class GpuRun:
         return {"params": self.params.cpu().numpy(), "grads": self.grads.cpu().numpy(),
                 "state": self.state.cpu().numpy(), "ns_out": self.ns_out.cpu().numpy()}
 
+    # -- per-entry device reads (no full-buffer copies) --
+    def dev_entry(self, i: int, what: str) -> np.ndarray:
+        """One entry of a device buffer as fp64: what in {"param", "grad",
+        "state", "state2", "o"}."""
+        t = self.torch
+        s = self.wl.specs[i]
+        if what in ("param", "grad"):
+            buf = self.params if what == "param" else self.grads
+            off, nb = self.offs[i], s.numel * s.itemsize
+            raw = buf[off:off + nb]
+            v = raw.view(t.bfloat16 if s.dtype == "bf16" else t.float32)
+        elif what in ("state", "state2"):
+            off = self.info[i].state_offset2 if what == "state2" else self.info[i].state_offset
+            v = self.state[off:off + 4 * s.numel].view(t.float32)
+        else:
+            off = self.info[i].ns_out_offset
+            v = self.ns_out[off:off + s.numel]
+        return v.float().cpu().numpy().astype(np.float64).reshape(s.rows, s.cols)
+
+    def snapshot_entries(self, idxs, what_list=("param", "grad", "state")):
+        self.torch.cuda.synchronize()
+        return {(i, w): self.dev_entry(i, w) for i in idxs for w in what_list}
+
+    def free(self) -> None:
+        for name in ("params", "grads", "state", "ws", "ns_out"):
+            setattr(self, name, None)
+        self.torch.cuda.empty_cache()
+
     # -- per-entry views of host copies --
     def param(self, snap, i) -> np.ndarray:
         s = self.wl.specs[i]

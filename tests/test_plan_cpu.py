@@ -1,0 +1,205 @@
+"""Host-side tests of the boundary: exported symbols, plan validation,
+routing, orientation and layout, and step argument checks that return before
+any HIP call.  No GPU is needed."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from matrix_optimizer_owner_amd import binding as B
+from matrix_optimizer_owner_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfsdp.h")
+CSRC = os.path.join(ROOT, "matrix_optimizer_owner_amd", "csrc")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mfsdp_status|const char\*)\s+(mfsdp_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert "mfsdp_plan_create" in names and "mfsdp_owner_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+        exported = set(re.findall(r"\bT (mfsdp_\w+)", out))
+        assert set(names) <= exported, set(names) - exported
+        assert set(B.EXPORTS) == set(names)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Sizes and field offsets of the ctypes mirrors equal a C compiler's."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "abi_sizes")
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_sizes.c"),
+                    "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    mirrors = {"mfsdp_entry": B.Entry, "mfsdp_hparams": B.Hparams, "mfsdp_entry_info": B.EntryInfo,
+               "mfsdp_step_args": B.StepArgs}
+    checked = 0
+    for line in filter(None, out):
+        key, val = line.split()
+        kind, name = key.split(":")
+        if kind == "sizeof":
+            assert ctypes.sizeof(mirrors[name]) == int(val), line
+        else:
+            struct, field = name.split(".")
+            assert getattr(mirrors[struct], field).offset == int(val), line
+        checked += 1
+    assert checked > 30
+
+
+def _plan(entries, pbytes=1 << 24, **hp):
+    return B.OwnerPlan(entries, pbytes, B.make_hparams(**hp))
+
+
+def _status(entries, pbytes=1 << 24, **hp):
+    try:
+        _plan(entries, pbytes, **hp)
+        return 0
+    except B.MfsdpError as e:
+        return e.status
+
+
+def test_validation_errors():
+    E = B.TableEntry
+    assert _status([E(0, 4, 4), E(16, 4, 4)]) == 2                   # overlap (4*4*2 = 32 bytes)
+    assert _status([E(8, 4, 4)]) == 3                                # misaligned
+    assert _status([E(0, -1, 4)]) == 1                               # negative dimension
+    assert _status([E(0, 1000, 1000)], pbytes=1000) == 1             # past the buffer
+    assert _status([E(0, 4, 4, dtype=7)]) == 4                       # dtype
+    assert _status([E(0, 4, 4, role=9)]) == 4                        # role
+    assert _status([E(0, 1 << 23, 1)], pbytes=1 << 30) == 4          # dimension above 2^22
+    assert _status([E(0, 4, 4)], ns_steps=-1) == 1
+    assert _status([E(0, 4, 4)], ns_steps=65) == 1
+    assert _status([E(0, 4, 4)], ns_precision=2) == 4
+    assert _status([E(0, 4, 4)], lr_scale_mode=3) == 4
+    assert _status([E(0, 4, 4)], lr=float("nan")) == 1
+    assert _status([E(0, 4, 4)], adam_beta2=1.0) == 1
+    assert _status([]) == 0                                          # empty table is legal
+    assert _status([E(0, 0, 5), E(0, 3, 0)]) == 0                    # empty shards never overlap
+
+
+def test_error_message_is_thread_local_text():
+    with pytest.raises(B.MfsdpError) as ei:
+        _plan([B.TableEntry(0, 4, 4), B.TableEntry(16, 4, 4)])
+    assert "overlap" in ei.value.message
+    assert B.load().mfsdp_status_string(2).decode() == "table entries overlap"
+
+
+def test_routing_orientation_and_scale():
+    E = B.TableEntry
+    p = _plan([E(0, 300, 700), E(1 << 20, 700, 300), E(2 << 20, 1, 64, B.F32), E(3 << 20, 64, 1, B.F32),
+               E(4 << 20, 5, 5, B.F32, B.ROLE_ADAMW), E(5 << 20, 1, 8, B.F32, B.ROLE_MUON), E(6 << 20, 0, 9)],
+              pbytes=8 << 20)
+    info = [p.entry_info(i) for i in range(7)]
+    assert [i.role for i in info] == [1, 1, 2, 2, 2, 1, -1]
+    assert (info[0].transposed, info[0].m, info[0].n) == (0, 300, 700)
+    assert (info[1].transposed, info[1].m, info[1].n) == (1, 300, 700)
+    assert info[0].lr_scale == 1.0 and info[1].lr_scale == pytest.approx(np.sqrt(7 / 3), rel=1e-7)
+    assert info[5].m == 1 and info[5].n == 8
+    p1 = _plan([E(0, 1024, 4096)], lr_scale_mode=1)
+    assert p1.entry_info(0).lr_scale == pytest.approx(0.2 * 64.0)
+    assert p.num_events() == 3 + 3 * 5
+    assert _plan([E(0, 4, 4)], ns_steps=0).num_events() == 3
+
+
+def test_state_and_ns_out_layout():
+    wl = W.small_ragged()
+    offs, pbytes = wl.layout()
+    dt = {"bf16": B.BF16, "f32": B.F32}
+    p = B.OwnerPlan([B.TableEntry(o, s.rows, s.cols, dt[s.dtype]) for o, s in zip(offs, wl.specs)], pbytes,
+                    B.make_hparams())
+    regions, ns = [], []
+    for i, s in enumerate(wl.specs):
+        inf = p.entry_info(i)
+        if inf.role == 1:
+            regions.append((inf.state_offset, s.numel * 4))
+            ns.append((inf.ns_out_offset, s.numel))
+        elif inf.role == 2:
+            regions += [(inf.state_offset, s.numel * 4), (inf.state_offset2, s.numel * 4)]
+    regions.sort()
+    for (a, n), (b, _) in zip(regions, regions[1:]):
+        assert a % 256 == 0 and a + n <= b
+    assert regions[-1][0] + regions[-1][1] <= p.state_bytes
+    ns.sort()
+    for (a, n), (b, _) in zip(ns, ns[1:]):
+        assert a % 64 == 0 and a + n <= b
+    assert ns[-1][0] + ns[-1][1] <= p.ns_out_elems
+
+
+@pytest.fixture(scope="module")
+def plan_checker(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("pc") / "plan_check")
+    cmd = [gxx, "-std=c++17", "-O1", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "plan.cpp"), os.path.join(ROOT, "tests", "plan_check.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    return exe
+
+
+def _table_text(wl):
+    offs, _ = wl.layout()
+    prec = int(wl.hparams.get("ns_precision", 0))
+    role = {"auto": 0, "muon": 1, "adamw": 2}
+    lines = [f"{prec} {len(wl.specs)}"]
+    for o, s in zip(offs, wl.specs):
+        lines.append(f"{o} {s.rows} {s.cols} {1 if s.dtype == 'bf16' else 0} {role[s.role]}")
+    return "\n".join(lines) + "\n"
+
+
+@pytest.mark.parametrize("name", ["small_ragged", "c0", "c1", "c2", "c3", "c4"])
+def test_plan_descriptor_invariants(plan_checker, name):
+    wl = W.small_ragged() if name == "small_ragged" else W.config(int(name[1]))
+    res = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("OK"), res.stdout
+
+
+def test_tile_override_keeps_invariants(plan_checker):
+    wl = W.config(1)
+    for t in ("128", "256", "256,128,256"):
+        res = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True,
+                             env=dict(os.environ, MFSDP_TILE=t))
+        assert res.returncode == 0, res.stdout
+
+
+def test_step_argument_checks_without_gpu():
+    """Every case here returns before the step touches HIP."""
+    lib = B.load()
+    p = _plan([B.TableEntry(0, 64, 64), B.TableEntry(8192, 1, 32, B.F32)])
+    ws = p.workspace_bytes
+
+    def st(**kw):
+        a = dict(params=4096, grads=4096, state=4096, workspace=4096, workspace_bytes=ws, step=1)
+        a.update(kw)
+        try:
+            p.step(a["params"], a["grads"], a["state"], a["workspace"], a["workspace_bytes"], a["step"],
+                   events=a.get("events", ()))
+            return 0
+        except B.MfsdpError as e:
+            return e.status
+
+    assert lib.mfsdp_owner_step(None, None) == 1
+    assert st(params=0) == 1
+    assert st(workspace=0) == 1
+    assert st(workspace=4096 + 8) == 1          # misaligned workspace
+    assert st(workspace_bytes=ws - 1) == 5
+    assert st(step=0) == 1                      # AdamW entry present
+    assert st(events=(1, 2)) == 1               # too few events
+    empty = _plan([B.TableEntry(0, 0, 8)])
+    empty.step(0, 0, 0, 0, 0, 0)                # nothing to do: returns OK without touching HIP
