@@ -2,9 +2,9 @@
 //
 //  * k_momentum: per 64x64 tile of a Muon matrix (natural layout, padded),
 //    m <- beta*m + g, u <- g + beta*m (Nesterov) or u <- m, written as the
-//    Newton-Schulz input in both layouts (X and X^T of the wide
-//    orientation; one store is direct, the other goes through LDS), plus the
-//    tile's sum of u^2.  "Muon ... orthogonalizing momentum-smoothed matrix
+//    Newton-Schulz input X0^T of the wide orientation (directly for a tall
+//    matrix, transposed through LDS for a wide one), plus the tile's sum of
+//    u^2.  "Muon ... orthogonalizing momentum-smoothed matrix
 //    updates" (MatrixFSDP, arXiv 2607.05895, Abstract).
 //  * k_norm_finalize: s = 1/(||U||_F + eps) per matrix, summing the tile
 //    partials in a fixed order (bitwise deterministic, no atomics).
@@ -58,11 +58,11 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
     const MatDesc d = a.mats[mi];
     const int local = blk - a.k1_begin[mi];
     const int tr = local / d.k1_tiles_c, tc = local % d.k1_tiles_c;
-    const int R = d.rows, C = d.cols;                // natural shape
-    const int ldn = d.transposed ? d.mp : d.np;      // padded natural column count
-    const int ldt = d.transposed ? d.np : d.mp;      // padded natural row count
-    T* natbuf = reinterpret_cast<T*>(a.ws + (d.transposed ? d.xt_off[0] : d.x_off));
-    T* trbuf = reinterpret_cast<T*>(a.ws + (d.transposed ? d.x_off : d.xt_off[0]));
+    const int R = d.rows, C = d.cols;  // natural shape
+    // X0^T (np x mp) is the natural layout of a tall matrix and the transpose
+    // of a wide one's
+    T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);
+    const bool tall = d.transposed != 0;
     const uint8_t* g = a.grads + d.param_off;
     float* mom = reinterpret_cast<float*>(a.state + d.mom_off);
     const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
@@ -116,22 +116,23 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
             }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            ss = __builtin_fmaf(u[k], u[k], ss);
-            tile[lr][tx * 8 + k] = u[k];
+        for (int k = 0; k < 8; ++k) ss = __builtin_fmaf(u[k], u[k], ss);
+        if (!tall) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tile[lr][tx * 8 + k] = u[k];
+        } else {
+            Vec8<T>::store(xt0 + int64_t(r) * d.mp + c0, u);
         }
-        Vec8<T>::store(natbuf + int64_t(r) * ldn + c0, u);
     }
-    __syncthreads();
-
-    // transposed copy: output row = natural column, 16 natural rows per thread
-    {
+    if (!tall) {
+        // transposed copy through LDS: X0^T row = natural column, 16 natural rows per thread
+        __syncthreads();
         const int oc = threadIdx.x >> 2;
         const int part = threadIdx.x & 3;
         float v[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) v[k] = tile[part * 16 + k][oc];
-        T* dst = trbuf + int64_t(tc * kK1Tile + oc) * ldt + tr * kK1Tile + part * 16;
+        T* dst = xt0 + int64_t(tc * kK1Tile + oc) * d.mp + tr * kK1Tile + part * 16;
         Vec8<T>::store(dst, v);
         Vec8<T>::store(dst + 8, v + 8);
     }
@@ -178,15 +179,16 @@ __global__ __launch_bounds__(256) void k_final_from_x(FinalArgs a) {
     const MatDesc d = a.mats[mi];
     const int local = blk - a.k1_begin[mi];
     const int tr = local / d.k1_tiles_c, tc = local % d.k1_tiles_c;
-    const int ldn = d.transposed ? d.mp : d.np;
-    const T* natbuf = reinterpret_cast<const T*>(a.ws + (d.transposed ? d.xt_off[0] : d.x_off));
+    const T* xt0 = reinterpret_cast<const T*>(a.ws + d.x_off[0]);
     const float s = a.s[mi];
     const float step = a.lr * d.lr_scale;
     uint8_t* w = a.params + d.param_off;
     for (int e = threadIdx.x; e < kK1Tile * kK1Tile; e += 256) {
         const int r = tr * kK1Tile + (e >> 6), c = tc * kK1Tile + (e & 63);
         if (r >= d.rows || c >= d.cols) continue;
-        const float o = s * Store<T>::load(natbuf + int64_t(r) * ldn + c);
+        // natural (r, c) is X0^T[r][c] for a tall matrix, X0^T[c][r] for a wide one
+        const int64_t xi = d.transposed ? int64_t(r) * d.mp + c : int64_t(c) * d.mp + r;
+        const float o = s * Store<T>::load(xt0 + xi);
         const int64_t idx = int64_t(r) * d.cols + c;
         const float wv = load_elem(w, d.dtype, idx);
         store_elem(w, d.dtype, idx, __builtin_fmaf(-step, o, __builtin_fmaf(-a.lrwd, wv, wv)));

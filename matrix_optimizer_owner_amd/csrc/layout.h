@@ -7,17 +7,16 @@
 //                 Tile upd[], TailDesc[n_tail], tail_begin[n_tail+1]
 //   [s]         float[n_mat]: 1/(||U||_F + eps) per Muon matrix
 //   [partials]  float[n_k1_blocks]: sum of u^2 over one 64x64 tile
-//   per matrix: X (mp x np), XT0 and XT1 (np x mp), A and B (mp x mp) in the
+//   per matrix: XT0 and XT1 (np x mp, ping-pong), A and B (mp x mp) in the
 //               Newton-Schulz storage type (bf16 or fp32), row-major.
 //
 // Orientation: every Muon matrix is handled as X (m x n, m <= n).  A tall
 // matrix (rows > cols) is stored transposed.  m and n are padded to
 // multiples of kPad with zeros; the zeros stay zero through every
 // Newton-Schulz iteration (rows and columns of zeros map to zeros), so the
-// contraction kernels need no bounds checks.  X is kept in both layouts: X
-// row-major feeds the Gram X X^T, X^T row-major (XT) feeds B X as the second
-// operand of a product whose operands are both contiguous along the
-// contraction index.
+// contraction kernels need no bounds checks.  X is kept only as X^T
+// (row-major n x m): the update reads it along its rows (the contraction
+// index m), the Gram reads it K-major through the transposing LDS read.
 #pragma once
 #include <stdint.h>
 
@@ -36,8 +35,8 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 struct MatDesc {
     uint64_t param_off;    // bytes into params and grads
     uint64_t mom_off;      // bytes into state (fp32 momentum, rows x cols)
-    uint64_t x_off;        // bytes into workspace: X  (mp x np)
-    uint64_t xt_off[2];    // bytes into workspace: XT ping-pong (np x mp)
+    uint64_t x_off[2];     // bytes into workspace: X^T ping-pong (np x mp, row-major)
+    uint64_t pad_off;      // unused (keeps the descriptor 8-byte fields in place)
     uint64_t a_off;        // bytes into workspace: A  (mp x mp)
     uint64_t b_off;        // bytes into workspace: B  (mp x mp)
     uint64_t ns_out_off;   // element offset into ns_out (fp32, rows x cols)

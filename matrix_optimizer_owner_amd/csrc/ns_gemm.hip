@@ -2,14 +2,16 @@
 //
 // Muon orthogonalises the momentum-smoothed update with Newton-Schulz
 // (MatrixFSDP, arXiv 2607.05895, Abstract).  One quintic iteration on the
-// wide X (m x n, m <= n) is three products, each an "NT" product
-// C = P Q^T whose operands are both row-major along the contraction index:
+// wide X (m x n, m <= n, row-major) is three products C = P Q^T:
 //
-//   Gram     A = X X^T           P = Q = X   (K = n)   upper tiles, mirrored
-//   poly     B = b A + c A A^T   P = Q = A   (K = m)   upper tiles, mirrored
+//   Gram     A = X X^T           P = Q = X, read K-major from X^T (its rows
+//                                are the contraction index); K = n; upper
+//                                tiles only, each stored with its mirror
+//   poly     B = b A + c A A^T   P = Q = A; K = m; upper tiles, mirrored
 //                                (A is symmetric, so A A = A A^T)
-//   update   X' = a X + B X      P = B, Q = X^T (K = m) all tiles; X' is
-//                                written row-major (in place) and transposed
+//   update   X' = a X + B X      P = B, Q = X^T (both row-major along the
+//                                contraction); all tiles; X'^T goes to the
+//                                other X^T buffer
 //   final    the last update writes W <- W (1 - lr wd) - lr*scale*O instead
 //            (O = X' in W's own orientation) and optionally O in fp32.
 //
@@ -18,14 +20,16 @@
 //
 // Every launch covers every matrix of the owner buffer: the block index
 // selects a tile from a host-built list sorted longest-contraction first.
-// Block: 256 threads = 4 wave64s in a 2x2 grid over a 256x256 output tile
-// (one wave per SIMD, each wave 128x128 as 4x4 MFMA 32x32 tiles) or a
-// 128x128 tile (two blocks per CU) for phases with too few large tiles to
-// fill the chip.  Operands stream through LDS in 128-byte rows (64 bf16 or
-// 32 fp32 of the contraction index per stage), double-buffered, with an XOR
-// swizzle of the 16-byte granules so that the MFMA fragment reads (16 bytes
-// per lane, 32 consecutive rows) spread over all banks.  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses
-// v_mfma_f32_32x32x2_f32, four per 8-element granule pair.
+// 256x256 output tiles with 8 wave64s (two per SIMD, each 128x64 as 4x2
+// MFMA 32x32 tiles), or 128x128 tiles with 4 waves (two blocks per CU) for
+// phases with too few large tiles to fill the chip.  Operands reach LDS by
+// direct global->LDS loads in 128-byte rows (64 bf16 or 32 fp32 of the
+// contraction index per stage), double-buffered.  Operands that are
+// contiguous along the contraction are read back with 16-byte fragment
+// reads; the Gram's K-major X^T is read back with the transposing LDS read
+// (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
+// v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
+// 8-element granule pair).
 #include "device_util.h"
 #include "kernels.h"
 
@@ -45,20 +49,18 @@ struct GemmArgs {
     float lrwd;         // lr * weight_decay
     float lr;
     int first;          // first iteration: scale by s (Gram: s^2)
-    int xt_in, xt_out;  // XT ping-pong buffers read / written by the update
+    int x_in, x_out;    // X^T ping-pong buffers read / written by the iteration
     int n_tiles;        // tiles in the list; a block walks tiles blockIdx.x + k*gridDim.x
 };
 
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
-    static constexpr int kSteps = 1;  // MFMA instructions per call
     __device__ __forceinline__ static void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
     }
 };
 template <> struct Mfma<float> {
-    static constexpr int kSteps = 4;
     __device__ __forceinline__ static void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -66,8 +68,7 @@ template <> struct Mfma<float> {
     }
 };
 
-// Four consecutive elements of the storage type (the 4 accumulator rows one
-// lane holds, read or written along the transposed layout).
+// Four consecutive elements of the storage type.
 template <typename T> struct Vec4;
 template <> struct Vec4<uint16_t> {
     typedef uint2 raw;
@@ -76,10 +77,10 @@ template <> struct Vec4<uint16_t> {
         const uint32_t w = (e < 2) ? r.x : r.y;
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
-    __device__ __forceinline__ static void store(uint16_t* p, float v0, float v1, float v2, float v3) {
+    __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[4]) {
         uint2 w;
-        w.x = uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16);
-        w.y = uint32_t(f32_to_bf16(v2)) | (uint32_t(f32_to_bf16(v3)) << 16);
+        w.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        w.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
         *reinterpret_cast<uint2*>(p) = w;
     }
 };
@@ -89,8 +90,8 @@ template <> struct Vec4<float> {
     __device__ __forceinline__ static float get(const raw& r, int e) {
         return e == 0 ? r.x : (e == 1 ? r.y : (e == 2 ? r.z : r.w));
     }
-    __device__ __forceinline__ static void store(float* p, float v0, float v1, float v2, float v3) {
-        *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+    __device__ __forceinline__ static void store(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     }
 };
 
@@ -107,21 +108,20 @@ template <> struct Param<float> {
 // 4x4 transpose inside each quad of lanes (lanes 4g..4g+3): on entry lane
 // 4g+j holds v[i] = element (row i, column j) of a 4x4 block; on exit it
 // holds v[i] = element (row j, column i).  Three DPP quad permutations (xor
-// 1, 2, 3); no LDS.  Turns the MFMA layout (4 consecutive rows per lane) into
-// 4 consecutive columns per lane for row-major stores.
+// 1, 2, 3); no LDS.  Converts between the MFMA accumulator layout (4
+// consecutive rows per lane) and 4 consecutive columns per lane.
 template <int CTRL>
 __device__ __forceinline__ float quad_xor(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 __device__ __forceinline__ void quad_transpose(float (&v)[4], int j) {
-    // round t: send v[j ^ t] to lane j ^ t; receive the partner's v[j], which is
-    // the output element at index j ^ t
-    float out[4];
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];  // t = 0 keeps v[j] at index j
+    // round t: send v[j ^ t] to lane j ^ t; receive the partner's v[j], which
+    // is the output element at index j ^ t
     const float s1 = v[j ^ 1], s2 = v[j ^ 2], s3 = v[j ^ 3];
     const float r1 = quad_xor<0xB1>(s1);  // quad_perm [1,0,3,2]
     const float r2 = quad_xor<0x4E>(s2);  // quad_perm [2,3,0,1]
     const float r3 = quad_xor<0x1B>(s3);  // quad_perm [3,2,1,0]
+    float out[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = i ^ j;  // which round delivers output index i
@@ -132,12 +132,28 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int j) {
 
 constexpr int kGran = 8;  // 16-byte granules per LDS row (128 bytes of contraction index)
 
-// Physical granule of logical granule g in LDS row `row` (128-byte rows):
-// g ^ ((row / 2) % 8).  Among the alternatives measured with the
-// SQ_LDS_BANK_CONFLICT counter on gfx950 (row % 8, (row + row/8) % 8,
-// (row/4) % 8, none, ...), this one gives zero bank conflicts for the
-// 16-byte-per-lane fragment reads of 32 consecutive rows.
+// Physical granule of logical granule g in LDS row `row`, for tiles stored
+// row-major along the contraction (16-byte fragment reads of 32 consecutive
+// rows): g ^ ((row / 2) % 8).  For K-major tiles read with transposing reads
+// (4 consecutive rows x 32 bytes per 16 lanes): g ^ (((row % 4) * 2) |
+// ((row / 4) % 2)).  Both were chosen among alternatives by measuring
+// SQ_LDS_BANK_CONFLICT on gfx950: zero conflicts.
 __device__ __forceinline__ int swz(int row, int g) { return g ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_k(int row, int g) { return g ^ (((row & 3) << 1) | ((row >> 2) & 1)); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte words addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4 (confirmed by an in-bounds probe on gfx950).  So if lane s of a
+// group addresses (k0 + s/4, c0 + 4*(s%4)) of a K-major tile, lane i gets
+// the 4 consecutive k0..k0+3 of column c0 + i.
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint8_t* lds_byte_addr) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(lds_byte_addr));
+    return __builtin_bit_cast(u32x2_t, v);
+}
 
 // Block shape: BT x BT output tile, NW wave64s in a 2 x (NW/2) grid; a wave
 // owns a (BT/2) x (2*BT/NW) block of MFMA 32x32 tiles.
@@ -161,6 +177,15 @@ struct FinalLds {
     static constexpr int PN = BT + 4;
     static constexpr int PT = HR + 4;
     static constexpr int FLOATS = HR * PN > BT * PT ? HR * PN : BT * PT;
+};
+
+template <int PHASE, int BT>
+struct LdsBytes {
+    // main loop: [stage][operand P/Q][row][granule]; the final epilogue reuses
+    // the same bytes (slightly more of them) for its O tile
+    static constexpr int main_loop = 2 * 2 * BT * kGran * 16;
+    static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
+    static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
 };
 
 // W <- W - lr*wd*W - step*O for n consecutive elements (n <= 4), as one
@@ -204,11 +229,10 @@ __device__ __forceinline__ void w_update4(WT_* w, float* o_out, const float* o, 
 // Last Newton-Schulz update fused with the parameter write:
 // O = (a X + B X) [* s on a first iteration], then W <- W - lr*wd*W -
 // lr*scale*O in W's own orientation and O optionally exported in fp32.
-// In two halves of the tile's rows: every lane writes its O values into an
-// LDS tile laid out in W's orientation, then the block walks that tile in W's
-// memory order with 4-element vectors (coalesced W loads and stores).  X comes
-// from its transposed copy XT, whose 4 consecutive elements are the 4 rows a
-// lane holds.
+// In two halves of the tile's rows: every lane reads X from X^T (its 4
+// accumulator rows are 4 consecutive elements there), writes O into an LDS
+// tile laid out in W's orientation, then the block walks that tile in W's
+// memory order with 4-element vectors (coalesced W loads and stores).
 template <typename T, int BT, int NW>
 __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                              const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
@@ -224,6 +248,7 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     uint8_t* Wb = a.params + d.param_off;
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;
     const int w_rows = d.rows, w_cols = d.cols;
+    const int j = frow & 3;
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -253,8 +278,9 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
                     if (tr) {
                         *reinterpret_cast<float4*>(olds + lc * L::PT + lr) = make_float4(o[0], o[1], o[2], o[3]);
                     } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) olds[(lr + e) * L::PN + lc] = o[e];
+                        quad_transpose(o, j);  // row lr + j, columns lc - j .. lc - j + 3
+                        *reinterpret_cast<float4*>(olds + (lr + j) * L::PN + (lc - j)) =
+                            make_float4(o[0], o[1], o[2], o[3]);
                     }
                 }
         }
@@ -300,14 +326,16 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
 // Scheduling groups for one stage of the main loop (bf16): sub-step 0 issues
 // the next stage's direct-to-LDS loads and sub-step 1's fragment reads among
 // its MFMAs, sub-steps 1 and 2 the following fragment reads, sub-step 3 only
-// MFMAs.
+// MFMAs.  NDS is the number of LDS read instructions per sub-step.
 template <int NMF, int NDS, int NVM>
 __device__ __forceinline__ void stage_schedule() {
-    constexpr int mf = NMF / NDS, vm = NVM / NDS;
-    constexpr int mf_tail = NMF - mf * NDS, vm_tail = NVM - vm * NDS;
+    constexpr int mf = NMF / NDS > 0 ? NMF / NDS : 1;
+    constexpr int groups = NMF / mf < NDS ? NMF / mf : NDS;  // groups that carry an MFMA
+    constexpr int vm = NVM / NDS;
+    constexpr int mf_tail = NMF - mf * groups, vm_tail = NVM - vm * NDS;
 #pragma unroll
     for (int t = 0; t < NDS; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);  // MFMA
+        if (t < groups) __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);  // MFMA
         if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM read
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
@@ -317,7 +345,7 @@ __device__ __forceinline__ void stage_schedule() {
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
         for (int t = 0; t < NDS; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);
+            if (t < groups) __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
@@ -325,33 +353,27 @@ __device__ __forceinline__ void stage_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
 }
 
-template <int PHASE, int BT>
-struct LdsBytes {
-    // main loop: [stage][operand P/Q][row][granule]; the final epilogue reuses
-    // the same bytes (slightly more of them) for its O tile
-    static constexpr int main_loop = 2 * 2 * BT * kGran * 16;
-    static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
-    static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
-};
-
 // C = P Q^T over one BT x BT output tile, then the phase's epilogue.
 template <typename T, int PHASE, int BT, int NW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uint8_t* lds_raw) {
     using S = Shape<BT, NW>;
     constexpr int MM = S::MM, MN = S::MN, LP = S::LP;
+    // the Gram's operands are K-major (X^T rows are the contraction index)
+    constexpr bool KM = PHASE == kGram;
     auto& lds = *reinterpret_cast<u32x4_t(*)[2][2][BT][kGran]>(lds_raw);
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
     const int mp = d.mp, np = d.np;
     const int row0 = int(tile.ti) * BT, col0 = int(tile.tj) * BT;
+    const T* XTin = reinterpret_cast<const T*>(a.ws + (a.x_in ? d.x_off[1] : d.x_off[0]));
 
     const T* P;
     const T* Q;
     int ldp, ldq, K;
     if (PHASE == kGram) {
-        P = Q = reinterpret_cast<const T*>(a.ws + d.x_off);
-        ldp = ldq = np;
+        P = Q = XTin;
+        ldp = ldq = mp;
         K = np;
     } else if (PHASE == kPoly) {
         P = Q = reinterpret_cast<const T*>(a.ws + d.a_off);
@@ -359,7 +381,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         K = mp;
     } else {
         P = reinterpret_cast<const T*>(a.ws + d.b_off);
-        Q = reinterpret_cast<const T*>(a.ws + (a.xt_in ? d.xt_off[1] : d.xt_off[0]));
+        Q = XTin;
         ldp = ldq = mp;
         K = mp;
     }
@@ -374,15 +396,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
     for (int i = 0; i < MM; ++i)
 #pragma unroll
-        for (int j = 0; j < MN; ++j)
+        for (int jj = 0; jj < MN; ++jj)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
 
     // Operand tiles reach LDS by direct global->LDS loads (16 bytes per lane):
     // one wave instruction fills 1 KB = 8 LDS rows, lane l landing at byte
     // 16*l, i.e. row l/8, physical granule l%8.  The swizzle is applied on the
     // global side: the lane fetches the logical granule stored there.  Wave w
     // fills row groups i*NW + w, i = 0 .. LP-1, of each operand.
+    // A K-major operand (the Gram's X^T) is stored as BT/KS column blocks of
+    // KS LDS rows: LDS row R = block*KS + k holds the 128 bytes of X^T row k,
+    // columns [block*KS, block*KS + KS) of the tile.
+    constexpr int KS = 128 / int(sizeof(T));  // contraction indices per stage (also columns per block)
+    constexpr int GE = 16 / int(sizeof(T));   // elements per granule
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int lr8 = lane >> 3, lq = lane & 7;
     const int64_t ldpb = int64_t(ldp) * int64_t(sizeof(T));
@@ -394,13 +421,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
         for (int i = 0; i < LP; ++i) {
             const int row = (i * NW + wave_u) * 8 + lr8;
-            const int64_t off = koff + swz(row, lq) * 16;
-            __builtin_amdgcn_global_load_lds(pl + int64_t(i) * NW * 8 * ldpb + off,
-                                             (__attribute__((address_space(3))) void*)&lds[st][0][(i * NW + wave_u) * 8][0],
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(ql + int64_t(i) * NW * 8 * ldqb + off,
-                                             (__attribute__((address_space(3))) void*)&lds[st][1][(i * NW + wave_u) * 8][0],
-                                             16, 0, 0);
+            auto* dstP = (__attribute__((address_space(3))) void*)&lds[st][0][(i * NW + wave_u) * 8][0];
+            auto* dstQ = (__attribute__((address_space(3))) void*)&lds[st][1][(i * NW + wave_u) * 8][0];
+            if constexpr (KM) {
+                const int blk = row / KS, k = row % KS;
+                const int64_t krow = int64_t(kt) * KS + k;
+                const int cofs = blk * KS + swz_k(row, lq) * GE;
+                __builtin_amdgcn_global_load_lds(P + krow * ldp + row0 + cofs, dstP, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(Q + krow * ldq + col0 + cofs, dstQ, 16, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds(pl + int64_t(i) * NW * 8 * ldpb + koff + swz(row, lq) * 16, dstP,
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(ql + int64_t(i) * NW * 8 * ldqb + koff + swz(row, lq) * 16, dstQ,
+                                                 16, 0, 0);
+            }
         }
     };
 
@@ -409,6 +443,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // Fragment of a 32-column MFMA tile starting at local column c of a
+    // K-major tile: bf16, two transposing reads (k0..k0+3 and k0+4..k0+7);
+    // fp32, four scalar reads.  Lane l needs column c + l%32 and the
+    // contraction indices of its MFMA half l/32.
+    auto kmajor_frag = [&](int s, int op, int c, int kk) -> u32x4_t {
+        const uint8_t* base = lds_raw + size_t((s * 2 + op) * BT) * 128;
+        if constexpr (sizeof(T) == 2) {
+            const int g16 = lane >> 4, sl = lane & 15;
+            const int col = c + 16 * (g16 & 1) + 4 * (sl & 3);   // this lane's source column
+            const int k = kk * 16 + 8 * (g16 >> 1) + (sl >> 2);  // this lane's source row
+            const int r0 = (col / KS) * KS + k, r1 = r0 + 4;
+            const int gr = (col % KS) / GE, e = (col % GE) * 2;
+            const u32x2_t lo = ds_read_tr16(base + r0 * 128 + swz_k(r0, gr) * 16 + e);
+            const u32x2_t hi = ds_read_tr16(base + r1 * 128 + swz_k(r1, gr) * 16 + e);
+            return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            const int col = c + frow;
+            const int k = kk * 8 + 4 * fhalf;
+            const int gr = (col % KS) / GE, e = (col % GE) * 4;
+            u32x4_t out;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = (col / KS) * KS + k + t;
+                out[t] = *reinterpret_cast<const uint32_t*>(base + r * 128 + swz_k(r, gr) * 16 + e);
+            }
+            return out;
+        }
+    };
+    auto frags = [&](int s, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
+        if constexpr (KM) {
+#pragma unroll
+            for (int i = 0; i < MM; ++i) af[i] = kmajor_frag(s, 0, wm * S::WTM + i * 32, kk);
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) bf[jj] = kmajor_frag(s, 1, wn * S::WTN + jj * 32, kk);
+        } else {
+#pragma unroll
+            for (int i = 0; i < MM; ++i) {
+                const int ra = wm * S::WTM + i * 32 + frow;
+                af[i] = lds[s][0][ra][swz(ra, 2 * kk + fhalf)];
+            }
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) {
+                const int rb = wn * S::WTN + jj * 32 + frow;
+                bf[jj] = lds[s][1][rb][swz(rb, 2 * kk + fhalf)];
+            }
+        }
+    };
+    auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
+#pragma unroll
+        for (int i = 0; i < MM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[i][jj], af[i], bf[jj]);
+    };
+
     // Per stage: 4 contraction sub-steps (16 bf16 each) of MM x MN MFMA steps,
     // fragments double-buffered across sub-steps.  Software pipeline across
     // stages: the MFMAs of a stage's last sub-step (operands already in
@@ -416,29 +504,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     // latency of the next stage's first fragments.  The loop body has no
     // branch: the first deferred group multiplies zero fragments, and the last
     // stage's look-ahead load and read hit the idle buffer.
-    auto frags = [&](int s, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
-#pragma unroll
-        for (int i = 0; i < MM; ++i) {
-            const int ra = wm * S::WTM + i * 32 + frow;
-            af[i] = lds[s][0][ra][swz(ra, 2 * kk + fhalf)];
-        }
-#pragma unroll
-        for (int j = 0; j < MN; ++j) {
-            const int rb = wn * S::WTN + j * 32 + frow;
-            bf[j] = lds[s][1][rb][swz(rb, 2 * kk + fhalf)];
-        }
-    };
-    auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
-#pragma unroll
-        for (int i = 0; i < MM; ++i)
-#pragma unroll
-            for (int j = 0; j < MN; ++j) Mfma<T>::step(acc[i][j], af[i], bf[j]);
-    };
     u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
 #pragma unroll
     for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < MN; ++j) fb1[j] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
     frags(0, 0, fa0, fb0);
     for (int kt = 0; kt < KT; ++kt) {
         const int s = kt & 1;
@@ -450,7 +520,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         mfmas(fa1, fb1);          // sub-step 1
         frags(s, 3, fa1, fb1);
         mfmas(fa0, fb0);          // sub-step 2
-        if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, MM + MN, 2 * LP>();
+        if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), 2 * LP>();
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         frags(s ^ 1, 0, fa0, fb0);  // next stage's first fragments
@@ -459,41 +529,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 
     // ---- epilogue ----
     // Accumulator element e of the 32x32 MFMA tile (mi, ni) holds
-    // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32.
+    // row 8*(e/4) + 4*(lane/32) + e%4, column lane%32.  After a quad
+    // transpose, lane 4g+j holds row (that row group) + j, columns 4g..4g+3.
     const float s1 = a.first ? a.s[tile.mat] : 1.f;
-    const bool diag = tile.ti == tile.tj;
-    T* out = nullptr;
-    T* outT = nullptr;
-    int ldo = mp;
-    if (PHASE == kGram) {
-        out = outT = reinterpret_cast<T*>(a.ws + d.a_off);
-    } else if (PHASE == kPoly) {
-        out = outT = reinterpret_cast<T*>(a.ws + d.b_off);
-    } else if (PHASE == kUpdate) {
-        out = reinterpret_cast<T*>(a.ws + d.x_off);
-        outT = reinterpret_cast<T*>(a.ws + (a.xt_out ? d.xt_off[1] : d.xt_off[0]));
-        ldo = np;
-    }
-    // The epilogue operand (A for the polynomial, X for the update) is read
-    // from a transposed copy - A itself (symmetric) or XT - so that the 4 rows
-    // a lane holds are 4 consecutive elements: one vector load per row group,
-    // issued one MFMA row block ahead.
-    const T* Etr = PHASE == kPoly ? reinterpret_cast<const T*>(a.ws + d.a_off) : Q;
-
+    const int j = frow & 3;
     if constexpr (PHASE == kFinal) {
-        final_update<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, Etr,
+        final_update<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
                                 reinterpret_cast<float*>(lds_raw));
         return;
     } else {
+        const bool diag = tile.ti == tile.tj;
+        T* out;
+        int ldo;
+        if (PHASE == kGram) {
+            out = reinterpret_cast<T*>(a.ws + d.a_off);
+            ldo = mp;
+        } else if (PHASE == kPoly) {
+            out = reinterpret_cast<T*>(a.ws + d.b_off);
+            ldo = mp;
+        } else {
+            out = reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0]));
+            ldo = mp;
+        }
+        // Epilogue operand, read one MFMA row block ahead along a transposed
+        // layout, where the 4 rows of a lane are 4 consecutive elements: A
+        // itself for the polynomial (A is symmetric), X^T for the update.
+        const T* E = PHASE == kPoly ? reinterpret_cast<const T*>(a.ws + d.a_off) : XTin;
+        auto eaddr = [&](int mi, int ni, int q) -> const T* {
+            const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
+            const int c = col0 + wn * S::WTN + ni * 32 + frow;
+            return E + int64_t(c) * mp + rb;
+        };
         typename Vec4<T>::raw ev[2][MN][4];
         if (PHASE != kGram) {
 #pragma unroll
             for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                    ev[0][ni][q] = Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * S::WTM + q * 8 + fhalf * 4);
-                }
+                for (int q = 0; q < 4; ++q) ev[0][ni][q] = Vec4<T>::load(eaddr(0, ni, q));
         }
 #pragma unroll
         for (int mi = 0; mi < MM; ++mi) {
@@ -501,11 +573,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
                 for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                        ev[(mi + 1) & 1][ni][q] = Vec4<T>::load(Etr + int64_t(c) * mp + row0 + wm * S::WTM +
-                                                                (mi + 1) * 32 + q * 8 + fhalf * 4);
-                    }
+                    for (int q = 0; q < 4; ++q) ev[(mi + 1) & 1][ni][q] = Vec4<T>::load(eaddr(mi + 1, ni, q));
             }
 #pragma unroll
             for (int ni = 0; ni < MN; ++ni)
@@ -515,23 +583,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     const int c = col0 + wn * S::WTN + ni * 32 + frow;
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = acc[mi][ni][q * 4 + e];
-                        if (PHASE == kGram)
-                            v[e] = x * (s1 * s1);
-                        else if (PHASE == kPoly)
-                            v[e] = a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * x;
-                        else
-                            v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + x) * s1;
+                    for (int e = 0; e < 4; ++e) v[e] = acc[mi][ni][q * 4 + e];
+                    if (PHASE == kUpdate) {
+                        // X'^T: the 4 rows of this lane are consecutive in column c of X'^T
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + v[e]) * s1;
+                        Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
+                        continue;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] = PHASE == kGram ? v[e] * (s1 * s1)
+                                                  : a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * v[e];
+                        // mirror tile: the 4 rows of this lane are consecutive in column-major
+                        if (!diag) Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
+                        quad_transpose(v, j);
                     }
-                    // transposed store: the 4 rows of this lane are consecutive in outT
-                    if (PHASE == kUpdate || !diag)
-                        Vec4<T>::store(outT + int64_t(c) * mp + rb, v[0], v[1], v[2], v[3]);
-                    // row-major store: after a quad transpose lane 4g+j holds row rb+j,
-                    // columns 4g..4g+3 of this 32-column block
-                    const int j = frow & 3;
-                    quad_transpose(v, j);
-                    Vec4<T>::store(out + int64_t(rb + j) * ldo + (c - j), v[0], v[1], v[2], v[3]);
+                    Vec4<T>::store(out + int64_t(rb + j) * ldo + (c - j), v);
                 }
         }
     }
@@ -551,7 +619,7 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
 }
 
 // Wave count of the 256-tile kernels (4: one wave per SIMD with 128x128 each;
-// 8: two per SIMD with 128x64 each).
+// 8: two per SIMD with 128x64 each, measured faster).
 #ifndef MFSDP_WAVES_256
 #define MFSDP_WAVES_256 8
 #endif
@@ -583,8 +651,8 @@ hipError_t launch_phase(const WorkspaceMap& map, const mfsdp_hparams& hp, int it
     a.lrwd = float(double(hp.lr) * double(hp.weight_decay));
     a.lr = hp.lr;
     a.first = iter == 1 && phase != 1;  // the polynomial sees an already normalised A
-    a.xt_in = (iter - 1) & 1;
-    a.xt_out = iter & 1;
+    a.x_in = (iter - 1) & 1;
+    a.x_out = iter & 1;
     if (phase == 0) {
         a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_gram);
         launch_tiles<T, kGram>(a, map.n_gram, map.tile_gram, stream);

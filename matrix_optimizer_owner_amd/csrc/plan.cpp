@@ -325,9 +325,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             MatDesc& d = mats[k];
             const uint64_t xbytes = uint64_t(d.mp) * uint64_t(d.np) * uint64_t(es);
             const uint64_t abytes = uint64_t(d.mp) * uint64_t(d.mp) * uint64_t(es);
-            d.x_off = section(xbytes);
-            d.xt_off[0] = section(xbytes);
-            d.xt_off[1] = section(xbytes);
+            d.x_off[0] = section(xbytes);
+            d.x_off[1] = section(xbytes);
             d.a_off = section(abytes);
             d.b_off = section(abytes);
         }

@@ -86,9 +86,8 @@ int main() {
     for (int k = 0; k < w.n_mat; ++k) {
         const MatDesc& d = mats[k];
         const uint64_t xb = uint64_t(d.mp) * d.np * es_ns, ab = uint64_t(d.mp) * d.mp * es_ns;
-        regs.push_back({d.x_off, xb});
-        regs.push_back({d.xt_off[0], xb});
-        regs.push_back({d.xt_off[1], xb});
+        regs.push_back({d.x_off[0], xb});
+        regs.push_back({d.x_off[1], xb});
         regs.push_back({d.a_off, ab});
         regs.push_back({d.b_off, ab});
     }
