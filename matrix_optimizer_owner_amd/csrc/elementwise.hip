@@ -1,10 +1,9 @@
 // elementwise.hip - the bandwidth-bound phases of the owner step on gfx950.
 //
-//  * k_momentum: per 64x64 tile of a Muon matrix (natural layout, padded),
-//    m <- beta*m + g, u <- g + beta*m (Nesterov) or u <- m, written as the
-//    Newton-Schulz input X0^T of the wide orientation (directly for a tall
-//    matrix, transposed through LDS for a wide one), plus the tile's sum of
-//    u^2.  "Muon ... orthogonalizing momentum-smoothed matrix
+//  * k_momentum: per 128x128 tile of a Muon matrix (natural layout,
+//    padded), m <- beta*m + g, u <- g + beta*m (Nesterov) or u <- m, written
+//    as the Newton-Schulz input X0^T of the wide orientation (transposed in
+//    registers for a wide matrix), plus the tile's sum of u^2.  "Muon ... orthogonalizing momentum-smoothed matrix
 //    updates" (MatrixFSDP, arXiv 2607.05895, Abstract).
 //  * k_norm_finalize: s = 1/(||U||_F + eps) per matrix, summing the tile
 //    partials in a fixed order (bitwise deterministic, no atomics).
@@ -49,9 +48,15 @@ template <> struct Vec8<float> {
     }
 };
 
+// One block per kK1Tile x kK1Tile tile of the natural layout (padded); each
+// of the 256 threads owns an 8 x 8 sub-block: 8 row loads of 8 elements
+// (16 lanes cover 256 contiguous bytes of a row), the momentum update in
+// registers, then 8 stores of 8 elements to X0^T - along the natural rows for
+// a tall matrix (X0^T is its natural layout) or along the natural columns
+// for a wide one (the thread owns the whole 8 x 8 block, so the transpose
+// costs nothing).  Padding elements get u = 0.
 template <typename T>
 __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
-    __shared__ float tile[kK1Tile][kK1Tile + 1];
     __shared__ float red[4];
     const int blk = blockIdx.x;
     const int mi = upper_index(a.k1_begin, a.n_mat, blk);
@@ -59,82 +64,98 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
     const int local = blk - a.k1_begin[mi];
     const int tr = local / d.k1_tiles_c, tc = local % d.k1_tiles_c;
     const int R = d.rows, C = d.cols;  // natural shape
-    // X0^T (np x mp) is the natural layout of a tall matrix and the transpose
-    // of a wide one's
-    T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);
+    T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);  // np x mp
     const bool tall = d.transposed != 0;
     const uint8_t* g = a.grads + d.param_off;
     float* mom = reinterpret_cast<float*>(a.state + d.mom_off);
-    const int tx = threadIdx.x & 7, ty = threadIdx.x >> 3;
-    const bool vec_ok = (C & 7) == 0;
+    constexpr int SUB = 8, TPR = kK1Tile / SUB;  // threads per tile row of sub-blocks
+    const int tx = threadIdx.x % TPR, ty = threadIdx.x / TPR;
+    const int r0 = tr * kK1Tile + ty * SUB, c0 = tc * kK1Tile + tx * SUB;
+    const bool vec_ok = (C & 7) == 0 && c0 + SUB <= C;
+    float u[SUB][SUB];
     float ss = 0.f;
 
+    if (vec_ok && r0 + SUB <= R) {
+        // all loads of the sub-block first (g and m cannot alias, but the
+        // compiler cannot know that), then the arithmetic and the stores
+        uint4 graw[SUB];
+        float4 gf[SUB][2], mf[SUB][2];
+        float4* m4 = reinterpret_cast<float4*>(mom + int64_t(r0) * C + c0);
+        const int ld4 = C / 4;
+        if (d.dtype == kBF16) {
+            const uint4* g4 = reinterpret_cast<const uint4*>(g) + (int64_t(r0) * C + c0) / 8;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int lr = ty + 32 * pass;
-        const int r = tr * kK1Tile + lr;
-        const int c0 = tc * kK1Tile + tx * 8;
-        float u[8];
-        const int64_t base = int64_t(r) * C + c0;
-        if (r < R && vec_ok && c0 + 8 <= C) {
-            float gv[8], mv[8];
+            for (int i = 0; i < SUB; ++i) graw[i] = g4[int64_t(i) * (C / 8)];
+        } else {
+            const float4* g4 = reinterpret_cast<const float4*>(g) + (int64_t(r0) * C + c0) / 4;
+#pragma unroll
+            for (int i = 0; i < SUB; ++i) {
+                gf[i][0] = g4[int64_t(i) * ld4];
+                gf[i][1] = g4[int64_t(i) * ld4 + 1];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            mf[i][0] = m4[int64_t(i) * ld4];
+            mf[i][1] = m4[int64_t(i) * ld4 + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            float gv[8];
             if (d.dtype == kBF16) {
-                const uint4 raw = *reinterpret_cast<const uint4*>(g + base * 2);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+                const uint32_t w[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     gv[2 * k] = __uint_as_float(w[k] << 16);
                     gv[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
                 }
             } else {
-                const float4 g0 = reinterpret_cast<const float4*>(g + base * 4)[0];
-                const float4 g1 = reinterpret_cast<const float4*>(g + base * 4)[1];
-                gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w;
-                gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
+                gv[0] = gf[i][0].x; gv[1] = gf[i][0].y; gv[2] = gf[i][0].z; gv[3] = gf[i][0].w;
+                gv[4] = gf[i][1].x; gv[5] = gf[i][1].y; gv[6] = gf[i][1].z; gv[7] = gf[i][1].w;
             }
-            float4* mp4 = reinterpret_cast<float4*>(mom + base);
-            const float4 m0 = mp4[0], m1 = mp4[1];
-            mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
-            mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
+            float mv[8] = {mf[i][0].x, mf[i][0].y, mf[i][0].z, mf[i][0].w,
+                           mf[i][1].x, mf[i][1].y, mf[i][1].z, mf[i][1].w};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 mv[k] = __builtin_fmaf(a.beta, mv[k], gv[k]);
-                u[k] = a.nesterov ? __builtin_fmaf(a.beta, mv[k], gv[k]) : mv[k];
+                u[i][k] = a.nesterov ? __builtin_fmaf(a.beta, mv[k], gv[k]) : mv[k];
+                ss = __builtin_fmaf(u[i][k], u[i][k], ss);
             }
-            mp4[0] = make_float4(mv[0], mv[1], mv[2], mv[3]);
-            mp4[1] = make_float4(mv[4], mv[5], mv[6], mv[7]);
-        } else {
+            m4[int64_t(i) * ld4] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+            m4[int64_t(i) * ld4 + 1] = make_float4(mv[4], mv[5], mv[6], mv[7]);
+        }
+    } else {
+        // ragged edge of the matrix (or of the padded tile): element by element
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            const int r = r0 + i;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                u[k] = 0.f;
+                u[i][k] = 0.f;
                 if (r < R && c0 + k < C) {
-                    const float gk = load_elem(g, d.dtype, base + k);
-                    const float mk = __builtin_fmaf(a.beta, mom[base + k], gk);
-                    mom[base + k] = mk;
-                    u[k] = a.nesterov ? __builtin_fmaf(a.beta, mk, gk) : mk;
+                    const int64_t idx = int64_t(r) * C + c0 + k;
+                    const float gk = load_elem(g, d.dtype, idx);
+                    const float mk = __builtin_fmaf(a.beta, mom[idx], gk);
+                    mom[idx] = mk;
+                    u[i][k] = a.nesterov ? __builtin_fmaf(a.beta, mk, gk) : mk;
                 }
+                ss = __builtin_fmaf(u[i][k], u[i][k], ss);
             }
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ss = __builtin_fmaf(u[k], u[k], ss);
-        if (!tall) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) tile[lr][tx * 8 + k] = u[k];
-        } else {
-            Vec8<T>::store(xt0 + int64_t(r) * d.mp + c0, u);
-        }
     }
-    if (!tall) {
-        // transposed copy through LDS: X0^T row = natural column, 16 natural rows per thread
-        __syncthreads();
-        const int oc = threadIdx.x >> 2;
-        const int part = threadIdx.x & 3;
-        float v[16];
+    if (tall) {
+        // X0^T is the natural layout: natural row r -> X0^T row r
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = tile[part * 16 + k][oc];
-        T* dst = xt0 + int64_t(tc * kK1Tile + oc) * d.mp + tr * kK1Tile + part * 16;
-        Vec8<T>::store(dst, v);
-        Vec8<T>::store(dst + 8, v + 8);
+        for (int i = 0; i < SUB; ++i) Vec8<T>::store(xt0 + int64_t(r0 + i) * d.mp + c0, u[i]);
+    } else {
+        // X0^T row = natural column c0 + k, elements r0 .. r0 + 7
+#pragma unroll
+        for (int k = 0; k < SUB; ++k) {
+            float col[SUB];
+#pragma unroll
+            for (int i = 0; i < SUB; ++i) col[i] = u[i][k];
+            Vec8<T>::store(xt0 + int64_t(c0 + k) * d.mp + r0, col);
+        }
     }
 
     ss = wave_sum(ss);
@@ -184,7 +205,7 @@ __global__ __launch_bounds__(256) void k_final_from_x(FinalArgs a) {
     const float step = a.lr * d.lr_scale;
     uint8_t* w = a.params + d.param_off;
     for (int e = threadIdx.x; e < kK1Tile * kK1Tile; e += 256) {
-        const int r = tr * kK1Tile + (e >> 6), c = tc * kK1Tile + (e & 63);
+        const int r = tr * kK1Tile + e / kK1Tile, c = tc * kK1Tile + e % kK1Tile;
         if (r >= d.rows || c >= d.cols) continue;
         // natural (r, c) is X0^T[r][c] for a tall matrix, X0^T[c][r] for a wide one
         const int64_t xi = d.transposed ? int64_t(r) * d.mp + c : int64_t(c) * d.mp + r;

@@ -26,7 +26,7 @@ constexpr int kPad = 256;          // padding granule of m and n in the workspac
 constexpr int kTileSmall = 128;    // output tile edges of the contraction kernels
 constexpr int kTileLarge = 256;
 constexpr int kLargeTileMin = 512; // a phase uses 256-tiles when it has at least this many
-constexpr int kK1Tile = 64;        // tile edge of the momentum / transpose kernel
+constexpr int kK1Tile = 128;       // tile edge of the momentum kernel
 constexpr int kTailChunk = 2048;   // elements per AdamW block
 constexpr uint64_t kAlign = 256;
 
