@@ -50,8 +50,17 @@ struct GemmArgs {
     float lr;
     int first;          // first iteration: scale by s (Gram: s^2)
     int x_in, x_out;    // X^T ping-pong buffers read / written by the iteration
-    int n_tiles;        // tiles in the list; a block walks tiles blockIdx.x + k*gridDim.x
+    int n_tiles;        // tiles in the list (one block per tile)
 };
+
+// Wave-uniform copies (scalar registers) of values every lane agrees on.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename P>
+__device__ __forceinline__ P* uni_ptr(P* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<P*>((uint64_t(hi) << 32) | lo);
+}
 
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
@@ -130,16 +139,26 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int j) {
     v[0] = out[0]; v[1] = out[1]; v[2] = out[2]; v[3] = out[3];
 }
 
-constexpr int kGran = 8;  // 16-byte granules per LDS row (128 bytes of contraction index)
-
-// Physical granule of logical granule g in LDS row `row`, for tiles stored
-// row-major along the contraction (16-byte fragment reads of 32 consecutive
-// rows): g ^ ((row / 2) % 8).  For K-major tiles read with transposing reads
-// (4 consecutive rows x 32 bytes per 16 lanes): g ^ (((row % 4) * 2) |
-// ((row / 4) % 2)).  Both were chosen among alternatives by measuring
+// Physical granule of logical granule g in LDS row `row`.  Tiles stored
+// row-major along the contraction are read back with 16-byte fragment reads
+// of 32 consecutive rows.  With 128-byte rows (8 granules): g ^ ((row / 2) %
+// 8).  With 64-byte rows (4 granules) two rows share a 128-byte bank window;
+// the 2-bit mask (bit 1: row bit 2; bit 0: row bit 1 xor row bit 3) spreads
+// both 8 consecutive rows over a 128-byte window and 16 over 256 bytes.
+// K-major tiles (128-byte rows, read with transposing reads of 4 consecutive
+// rows x 32 bytes per 16 lanes): g ^ (((row % 4) * 2) | ((row / 4) % 2)).
+// The 128-byte forms were chosen among alternatives by measuring
 // SQ_LDS_BANK_CONFLICT on gfx950: zero conflicts.
-__device__ __forceinline__ int swz(int row, int g) { return g ^ ((row >> 1) & 7); }
+template <int GR>
+__device__ __forceinline__ int swz_r(int row, int g) {
+    if constexpr (GR == 8) return g ^ ((row >> 1) & 7);
+    else return g ^ ((((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1));
+}
 __device__ __forceinline__ int swz_k(int row, int g) { return g ^ (((row & 3) << 1) | ((row >> 2) & 1)); }
+
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no
+// swizzle, no index stride.
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -165,8 +184,42 @@ struct Shape {
     static constexpr int WTN = BT / WC;          // wave tile columns
     static constexpr int MM = WTM / 32;          // MFMA tiles per wave along rows
     static constexpr int MN = WTN / 32;          // MFMA tiles per wave along columns
-    static constexpr int LP = BT / (8 * NW);     // direct-to-LDS loads per wave, operand and stage
 };
+
+// Main-loop pipeline: stages of KSB bytes of contraction index (two MFMA
+// sub-steps of 32 bytes per 64), NBUF stage buffers in LDS, loads issued
+// NBUF - 1 stages ahead.
+template <int BT, int NW, int KSB, int NBUF>
+struct Pipe {
+    static constexpr int SUBS = KSB / 32;          // MFMA sub-steps per stage
+    static constexpr int GR = KSB / 16;            // 16-byte granules per row-major LDS row
+    static constexpr int OPB = BT * KSB;           // bytes of one operand's stage
+    static constexpr int LP = OPB / (1024 * NW);   // direct-to-LDS loads per wave, operand and stage
+    static constexpr int BYTES = NBUF * 2 * OPB;
+    static_assert(SUBS % 2 == 0 && LP >= 1 && OPB % (1024 * NW) == 0, "pipeline shape");
+    static_assert(NBUF >= 2 && 2 * LP * (NBUF - 2) <= 63, "vmcnt range");
+};
+
+// Stage geometry per tile edge: (KSB, NBUF).  128-byte stages, two buffers
+// (256 tiles: 128 KB; 128 tiles, two blocks per CU: 64 KB each).  On the
+// Llama-3-8B share, 64-byte stages with 3 to 5 buffers (more look-ahead, twice
+// the barriers) measured 16% slower, and the look-ahead depth made no
+// difference: the loop is not bound by load latency.
+#ifndef MFSDP_KSB_256
+#define MFSDP_KSB_256 128
+#endif
+#ifndef MFSDP_NBUF_256
+#define MFSDP_NBUF_256 2
+#endif
+#ifndef MFSDP_KSB_128
+#define MFSDP_KSB_128 128
+#endif
+#ifndef MFSDP_NBUF_128
+#define MFSDP_NBUF_128 2
+#endif
+template <int BT> struct PipeFor;
+template <> struct PipeFor<256> { static constexpr int KSB = MFSDP_KSB_256, NBUF = MFSDP_NBUF_256; };
+template <> struct PipeFor<128> { static constexpr int KSB = MFSDP_KSB_128, NBUF = MFSDP_NBUF_128; };
 
 // LDS tile of the final update (one half of the tile's rows at a time), in
 // W's orientation: [BT/2][BT+4] floats when W is not transposed, else
@@ -179,11 +232,11 @@ struct FinalLds {
     static constexpr int FLOATS = HR * PN > BT * PT ? HR * PN : BT * PT;
 };
 
-template <int PHASE, int BT>
+template <int PHASE, int BT, int NW>
 struct LdsBytes {
-    // main loop: [stage][operand P/Q][row][granule]; the final epilogue reuses
-    // the same bytes (slightly more of them) for its O tile
-    static constexpr int main_loop = 2 * 2 * BT * kGran * 16;
+    // main loop: [stage buffer][operand P/Q][KSB-byte rows]; the final
+    // epilogue reuses the same bytes for its O tile
+    static constexpr int main_loop = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>::BYTES;
     static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
     static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
 };
@@ -323,11 +376,13 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     }
 }
 
-// Scheduling groups for one stage of the main loop (bf16): sub-step 0 issues
-// the next stage's direct-to-LDS loads and sub-step 1's fragment reads among
-// its MFMAs, sub-steps 1 and 2 the following fragment reads, sub-step 3 only
-// MFMAs.  NDS is the number of LDS read instructions per sub-step.
-template <int NMF, int NDS, int NVM>
+// Scheduling groups for one stage of the main loop (bf16), in program order:
+// the stage's direct-to-LDS loads and the previous stage's deferred last
+// sub-step of MFMAs, interleaved with sub-step 1's fragment reads; then for
+// each further sub-step its MFMAs interleaved with the next fragment reads;
+// then the MFMAs of the second-to-last sub-step.  NDS is the number of LDS
+// read instructions per sub-step.
+template <int NMF, int NDS, int NVM, int SUBS>
 __device__ __forceinline__ void stage_schedule() {
     constexpr int mf = NMF / NDS > 0 ? NMF / NDS : 1;
     constexpr int groups = NMF / mf < NDS ? NMF / mf : NDS;  // groups that carry an MFMA
@@ -342,7 +397,7 @@ __device__ __forceinline__ void stage_schedule() {
     if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
     if constexpr (vm_tail > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm_tail, 0);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < SUBS - 2; ++r) {
 #pragma unroll
         for (int t = 0; t < NDS; ++t) {
             if (t < groups) __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);
@@ -353,14 +408,45 @@ __device__ __forceinline__ void stage_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier between ping-pong phases: the wave's LDS reads have returned
+// (the buffer they read may be refilled next phase), nothing is moved across.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+#ifndef MFSDP_PINGPONG
+#define MFSDP_PINGPONG 1
+#endif
+#ifndef MFSDP_PP_BURST
+#define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
+#endif
+// The ping-pong schedule serves the bf16 Gram on 256 tiles with 8 waves and
+// 128-byte stages in two buffers.  On the Llama-3-8B share it made the Gram
+// 7% faster (its transposing fragment reads are twice as many instructions,
+// which batch better than they interleave) and the row-major phases 5%
+// slower; half-stage bursts were slower for all three.
+template <typename T, int PHASE, int BT, int NW>
+struct PingPong {
+    static constexpr bool value = MFSDP_PINGPONG && sizeof(T) == 2 && PHASE == kGram && BT == 256 && NW == 8 &&
+                                  PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
+};
+
 // C = P Q^T over one BT x BT output tile, then the phase's epilogue.
 template <typename T, int PHASE, int BT, int NW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uint8_t* lds_raw) {
     using S = Shape<BT, NW>;
-    constexpr int MM = S::MM, MN = S::MN, LP = S::LP;
+    using PP = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>;
+    constexpr int MM = S::MM, MN = S::MN, LP = PP::LP, KSB = PipeFor<BT>::KSB, NBUF = PipeFor<BT>::NBUF;
+    constexpr int SUBS = PP::SUBS, GR = PP::GR, OPB = PP::OPB;
     // the Gram's operands are K-major (X^T rows are the contraction index)
     constexpr bool KM = PHASE == kGram;
-    auto& lds = *reinterpret_cast<u32x4_t(*)[2][2][BT][kGran]>(lds_raw);
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
@@ -401,93 +487,118 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
 
     // Operand tiles reach LDS by direct global->LDS loads (16 bytes per lane):
-    // one wave instruction fills 1 KB = 8 LDS rows, lane l landing at byte
-    // 16*l, i.e. row l/8, physical granule l%8.  The swizzle is applied on the
-    // global side: the lane fetches the logical granule stored there.  Wave w
-    // fills row groups i*NW + w, i = 0 .. LP-1, of each operand.
-    // A K-major operand (the Gram's X^T) is stored as BT/KS column blocks of
-    // KS LDS rows: LDS row R = block*KS + k holds the 128 bytes of X^T row k,
-    // columns [block*KS, block*KS + KS) of the tile.
-    constexpr int KS = 128 / int(sizeof(T));  // contraction indices per stage (also columns per block)
-    constexpr int GE = 16 / int(sizeof(T));   // elements per granule
+    // one wave instruction fills 1 KB of LDS, lane l landing at byte 16*l.
+    // Stage buffer b holds operand o at byte (2*b + o) * OPB.  A row-major
+    // operand is stored as BT rows of KSB bytes (its stage's slice of the
+    // contraction index); 1 KB holds RPK rows, lane l landing in row l/GR at
+    // physical granule l%GR.  The swizzle is applied on the global side: the
+    // lane fetches the logical granule stored there (the XOR is an
+    // involution).  A K-major operand (the Gram's X^T) is stored as BT/CB
+    // column blocks of KST rows of 128 bytes: LDS row R = block*KST + k holds
+    // X^T row k of the stage, columns [block*CB, block*CB + CB) of the tile.
+    // Wave w fills the 1 KB pieces i*NW + w, i = 0 .. LP-1, of each operand.
+    constexpr int GE = 16 / int(sizeof(T));     // elements per granule
+    constexpr int KST = KSB / int(sizeof(T));   // contraction indices per stage
+    constexpr int CB = 128 / int(sizeof(T));    // K-major: tile columns per 128-byte LDS row
+    constexpr int RPK = 1024 / KSB;             // row-major: LDS rows per 1 KB
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int lr8 = lane >> 3, lq = lane & 7;
-    const int64_t ldpb = int64_t(ldp) * int64_t(sizeof(T));
-    const int64_t ldqb = int64_t(ldq) * int64_t(sizeof(T));
-    const uint8_t* pl = reinterpret_cast<const uint8_t*>(P) + (int64_t(row0) + wave_u * 8 + lr8) * ldpb;
-    const uint8_t* ql = reinterpret_cast<const uint8_t*>(Q) + (int64_t(col0) + wave_u * 8 + lr8) * ldqb;
-    auto issue = [&](int kt, int st) {
-        const int64_t koff = int64_t(kt) * 128;
+    // The loads go through buffer resources over each operand's matrix
+    // buffer (the planner keeps every padded buffer below 2 GB): a per-lane
+    // 32-bit offset, the same for every load of the wave, plus a wave-uniform
+    // offset per load and stage.  For load i of wave w (piece i*NW + w), a
+    // row-major operand row is piece*RPK + lane/GR, whose bits below 4 (all
+    // the swizzle reads) do not depend on i; a K-major LDS row R = piece*8 +
+    // lane/8 has block R / KST and contraction index R % KST, whose lane part
+    // is lane/8.
+    static_assert((NW * RPK) % 16 == 0 && KST % 8 == 0, "load geometry");
+    constexpr int ES = int(sizeof(T));
+    uint32_t voff;
+    int uP[LP], uQ[LP];  // wave-uniform byte offsets of load i (stage 0)
+    int ldsd[LP];        // LDS byte offset of load i inside an operand's stage
+    if constexpr (KM) {
+        const int l8 = lane >> 3;
+        voff = uint32_t((l8 * ldp + swz_k(l8, lane & 7) * GE) * ES);
+    } else {
+        const int row = wave_u * RPK + lane / GR;
+        voff = uint32_t(row * ldp * ES + swz_r<GR>(row, lane % GR) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+        const int piece = i * NW + wave_u;
+        ldsd[i] = piece * 1024;
+        if constexpr (KM) {
+            const int blk = (piece * 8) / KST, k0 = (piece * 8) % KST;
+            uP[i] = uni((k0 * ldp + row0 + blk * CB) * ES);
+            uQ[i] = uni((k0 * ldq + col0 + blk * CB) * ES);
+        } else {
+            uP[i] = uni((row0 + i * NW * RPK) * ldp * ES);
+            uQ[i] = uni((col0 + i * NW * RPK) * ldq * ES);
+        }
+    }
+    // bytes of each operand's matrix buffer, and between consecutive stages
+    const int bytesP = (PHASE == kGram ? np : mp) * mp * ES;
+    const int bytesQ = (PHASE == kPoly ? mp : np) * mp * ES;
+    const int stepP = uni(KM ? KST * ldp * ES : KSB);
+    const int stepQ = uni(KM ? KST * ldq * ES : KSB);
+    // (the resources and wave offsets must live in scalar registers)
+    const __amdgpu_buffer_rsrc_t rsP =
+        __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(P)), 0, uni(bytesP), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsQ =
+        __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(Q)), 0, uni(bytesQ), kRsrcWord3);
+    auto issue = [&](int kt, int buf) {
+        const int kp = kt * stepP, kq = kt * stepQ;
 #pragma unroll
         for (int i = 0; i < LP; ++i) {
-            const int row = (i * NW + wave_u) * 8 + lr8;
-            auto* dstP = (__attribute__((address_space(3))) void*)&lds[st][0][(i * NW + wave_u) * 8][0];
-            auto* dstQ = (__attribute__((address_space(3))) void*)&lds[st][1][(i * NW + wave_u) * 8][0];
-            if constexpr (KM) {
-                const int blk = row / KS, k = row % KS;
-                const int64_t krow = int64_t(kt) * KS + k;
-                const int cofs = blk * KS + swz_k(row, lq) * GE;
-                __builtin_amdgcn_global_load_lds(P + krow * ldp + row0 + cofs, dstP, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(Q + krow * ldq + col0 + cofs, dstQ, 16, 0, 0);
-            } else {
-                __builtin_amdgcn_global_load_lds(pl + int64_t(i) * NW * 8 * ldpb + koff + swz(row, lq) * 16, dstP,
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(ql + int64_t(i) * NW * 8 * ldqb + koff + swz(row, lq) * 16, dstQ,
-                                                 16, 0, 0);
-            }
+            auto* dstP = (__attribute__((address_space(3))) void*)(lds_raw + (2 * buf) * OPB + ldsd[i]);
+            auto* dstQ = (__attribute__((address_space(3))) void*)(lds_raw + (2 * buf + 1) * OPB + ldsd[i]);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, dstP, 16, int(voff), uP[i] + kp, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, dstQ, 16, int(voff), uQ[i] + kq, 0, 0);
         }
     };
-
-    const int KT = K * int(sizeof(T)) / 128;  // stages of 128 bytes along the contraction index
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
 
     // Fragment of a 32-column MFMA tile starting at local column c of a
     // K-major tile: bf16, two transposing reads (k0..k0+3 and k0+4..k0+7);
     // fp32, four scalar reads.  Lane l needs column c + l%32 and the
     // contraction indices of its MFMA half l/32.
-    auto kmajor_frag = [&](int s, int op, int c, int kk) -> u32x4_t {
-        const uint8_t* base = lds_raw + size_t((s * 2 + op) * BT) * 128;
+    auto kmajor_frag = [&](int b, int op, int c, int kk) -> u32x4_t {
+        const uint8_t* base = lds_raw + (2 * b + op) * OPB;
         if constexpr (sizeof(T) == 2) {
             const int g16 = lane >> 4, sl = lane & 15;
             const int col = c + 16 * (g16 & 1) + 4 * (sl & 3);   // this lane's source column
             const int k = kk * 16 + 8 * (g16 >> 1) + (sl >> 2);  // this lane's source row
-            const int r0 = (col / KS) * KS + k, r1 = r0 + 4;
-            const int gr = (col % KS) / GE, e = (col % GE) * 2;
+            const int r0 = (col / CB) * KST + k, r1 = r0 + 4;
+            const int gr = (col % CB) / GE, e = (col % GE) * 2;
             const u32x2_t lo = ds_read_tr16(base + r0 * 128 + swz_k(r0, gr) * 16 + e);
             const u32x2_t hi = ds_read_tr16(base + r1 * 128 + swz_k(r1, gr) * 16 + e);
             return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         } else {
             const int col = c + frow;
             const int k = kk * 8 + 4 * fhalf;
-            const int gr = (col % KS) / GE, e = (col % GE) * 4;
+            const int gr = (col % CB) / GE, e = (col % GE) * 4;
             u32x4_t out;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int r = (col / KS) * KS + k + t;
+                const int r = (col / CB) * KST + k + t;
                 out[t] = *reinterpret_cast<const uint32_t*>(base + r * 128 + swz_k(r, gr) * 16 + e);
             }
             return out;
         }
     };
-    auto frags = [&](int s, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
+    auto rowmajor_frag = [&](int b, int op, int r, int kk) -> u32x4_t {
+        const uint8_t* base = lds_raw + (2 * b + op) * OPB;
+        return *reinterpret_cast<const u32x4_t*>(base + r * KSB + swz_r<GR>(r, 2 * kk + fhalf) * 16);
+    };
+    auto frags = [&](int b, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
         if constexpr (KM) {
 #pragma unroll
-            for (int i = 0; i < MM; ++i) af[i] = kmajor_frag(s, 0, wm * S::WTM + i * 32, kk);
+            for (int i = 0; i < MM; ++i) af[i] = kmajor_frag(b, 0, wm * S::WTM + i * 32, kk);
 #pragma unroll
-            for (int jj = 0; jj < MN; ++jj) bf[jj] = kmajor_frag(s, 1, wn * S::WTN + jj * 32, kk);
+            for (int jj = 0; jj < MN; ++jj) bf[jj] = kmajor_frag(b, 1, wn * S::WTN + jj * 32, kk);
         } else {
 #pragma unroll
-            for (int i = 0; i < MM; ++i) {
-                const int ra = wm * S::WTM + i * 32 + frow;
-                af[i] = lds[s][0][ra][swz(ra, 2 * kk + fhalf)];
-            }
+            for (int i = 0; i < MM; ++i) af[i] = rowmajor_frag(b, 0, wm * S::WTM + i * 32 + frow, kk);
 #pragma unroll
-            for (int jj = 0; jj < MN; ++jj) {
-                const int rb = wn * S::WTN + jj * 32 + frow;
-                bf[jj] = lds[s][1][rb][swz(rb, 2 * kk + fhalf)];
-            }
+            for (int jj = 0; jj < MN; ++jj) bf[jj] = rowmajor_frag(b, 1, wn * S::WTN + jj * 32 + frow, kk);
         }
     };
     auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
@@ -497,35 +608,111 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[i][jj], af[i], bf[jj]);
     };
 
-    // Per stage: 4 contraction sub-steps (16 bf16 each) of MM x MN MFMA steps,
-    // fragments double-buffered across sub-steps.  Software pipeline across
-    // stages: the MFMAs of a stage's last sub-step (operands already in
-    // registers) are issued after the stage barrier, so they cover the LDS
-    // latency of the next stage's first fragments.  The loop body has no
-    // branch: the first deferred group multiplies zero fragments, and the last
-    // stage's look-ahead load and read hit the idle buffer.
-    u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
-#pragma unroll
-    for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
-    frags(0, 0, fa0, fb0);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int s = kt & 1;
-        issue(kt + 1 < KT ? kt + 1 : kt, s ^ 1);
-        mfmas(fa1, fb1);          // sub-step 3 of the previous stage (zeros on the first)
-        frags(s, 1, fa1, fb1);
-        mfmas(fa0, fb0);          // sub-step 0
-        frags(s, 2, fa0, fb0);
-        mfmas(fa1, fb1);          // sub-step 1
-        frags(s, 3, fa1, fb1);
-        mfmas(fa0, fb0);          // sub-step 2
-        if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), 2 * LP>();
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int KT = K * int(sizeof(T)) / KSB;   // stages along the contraction index
+    if constexpr (!PingPong<T, PHASE, BT, NW>::value) {
+        // Ring of NBUF stage buffers: stage t lives in buffer t % NBUF and its
+        // loads are issued NBUF - 1 stages ahead, into the buffer the previous
+        // stage has just released (every wave passed the barrier that ended it).
+        // A wave waits only for its own loads of the next stage (loads complete
+        // in issue order), then the barrier makes every wave's loads visible.
+        // Past the last stage the look-ahead re-loads the last stage into the
+        // released buffer, which no later stage reads: the loop has no branch and
+        // the wait count stays fixed.  Inside a stage, SUBS sub-steps of MM x MN
+        // MFMA steps with fragments double-buffered across sub-steps; the last
+        // sub-step's MFMAs (operands already in registers) run after the stage
+        // barrier, covering the LDS latency of the next stage's first fragments
+        // (the first deferred group multiplies zero fragments).
+        constexpr int D = NBUF - 1;                // look-ahead in stages
+        constexpr int VM_STAGE = 2 * LP;           // loads per wave and stage
+    #pragma unroll
+        for (int t = 0; t < D; ++t) issue(t < KT ? t : KT - 1, t);
+        wait_vmcnt<VM_STAGE * (D - 1)>();
         __syncthreads();
-        frags(s ^ 1, 0, fa0, fb0);  // next stage's first fragments
+
+        u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
+    #pragma unroll
+        for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
+    #pragma unroll
+        for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
+        frags(0, 0, fa0, fb0);
+        int buf = 0;                 // buffer of stage kt
+        int lbuf = D;                // buffer receiving stage kt + D
+        for (int kt = 0; kt < KT; ++kt) {
+            issue(kt + D < KT ? kt + D : KT - 1, lbuf);
+            mfmas(fa1, fb1);  // last sub-step of the previous stage (zeros on the first)
+    #pragma unroll
+            for (int u = 1; u < SUBS; ++u) {
+                if (u & 1) {
+                    frags(buf, u, fa1, fb1);
+                    mfmas(fa0, fb0);  // sub-step u - 1
+                } else {
+                    frags(buf, u, fa0, fb0);
+                    mfmas(fa1, fb1);
+                }
+            }
+            if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), VM_STAGE, SUBS>();
+            wait_vmcnt<VM_STAGE * (D - 1)>();
+            __syncthreads();
+            buf = buf + 1 == NBUF ? 0 : buf + 1;
+            lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
+            frags(buf, 0, fa0, fb0);  // next stage's first fragments
+        }
+        mfmas(fa1, fb1);  // last sub-step of the last stage
+        wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
+    } else {
+        // Ping-pong.  Waves w and w + 4 share a SIMD (the hardware places a
+        // block's waves 0-3 on four different SIMDs and repeats that order for
+        // waves 4-7); group g = w / 4 thus holds one wave per SIMD.  The
+        // contraction runs in chunks of BURST sub-steps (CPS per stage) and in
+        // 2*NC + 1 phases separated by block barriers.  In phase p, group g
+        // reads every fragment of chunk (p - g)/2 from LDS into registers when
+        // p - g is even, and issues the MFMAs of the chunk it holds when p - g
+        // is odd: on each SIMD one wave multiplies back to back while the
+        // other fetches, and the roles swap every phase.  Stage s lives in
+        // buffer s % 2; all waves issue its direct-to-LDS loads in phase
+        // 2*CPS*(s - 1), once both groups have read stage s - 2 from that
+        // buffer, and wait for them at the end of phase 2*CPS*s - 1, before
+        // the barrier that lets group 0 read it.
+        constexpr int BURST = MFSDP_PP_BURST, CPS = SUBS / BURST;
+        static_assert(SUBS % BURST == 0, "burst");
+        const int g = wave_u >> 2;
+        const int NC = KT * CPS;
+        // the loads and waits that belong to phase p (same for every wave)
+        auto phase_loads = [&](int p) {
+            if (p % (2 * CPS) == 0 && p / (2 * CPS) + 1 < KT) issue(p / (2 * CPS) + 1, (p / (2 * CPS) + 1) & 1);
+        };
+        auto phase_end = [&](int p) {
+            if (p % (2 * CPS) == 2 * CPS - 1) wait_vmcnt<0>();
+            phase_barrier();
+        };
+        u32x4_t fa[BURST][MM], fb[BURST][MN];
+        issue(0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        // Every wave runs the same straight-line loop (fetch chunk c, then
+        // multiply it); group 1 runs it one phase later than group 0, so the
+        // accumulators never pass through a branch.
+        if (g == 1) {
+            phase_loads(0);
+            phase_end(0);
+        }
+        for (int c = 0; c < NC; ++c) {
+            const int p = 2 * c + g;
+            const int st = c / CPS, u0 = (c % CPS) * BURST;
+            phase_loads(p);
+#pragma unroll
+            for (int u = 0; u < BURST; ++u) frags(st & 1, u0 + u, fa[u], fb[u]);
+            phase_end(p);
+            phase_loads(p + 1);
+#pragma unroll
+            for (int u = 0; u < BURST; ++u) mfmas(fa[u], fb[u]);
+            phase_end(p + 1);
+        }
+        if (g == 0) {
+            phase_loads(2 * NC);
+            phase_end(2 * NC);
+        }
     }
-    mfmas(fa1, fb1);  // sub-step 3 of the last stage
 
     // ---- epilogue ----
     // Accumulator element e of the 32x32 MFMA tile (mi, ni) holds
@@ -606,16 +793,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 }
 
 // One block per tile: the hardware dispatcher then hands the cost-sorted
-// tile list to CUs as they free up (greedy longest-first).  A grid smaller
-// than the list would make each block walk tiles with a fixed stride; that
-// static split measured slower than dispatch on the Llama-3-8B share.
+// tile list to CUs as they free up (greedy longest-first).  A persistent grid
+// walking the list with a fixed stride measured slower on the Llama-3-8B
+// share.
 template <typename T, int PHASE, int BT, int NW>
 __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<PHASE, BT>::value];
-    for (int t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
-        gemm_tile<T, PHASE, BT, NW>(a, t, lds_raw);
-        __syncthreads();  // LDS free before the next tile's first loads
-    }
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<PHASE, BT, NW>::value];
+    gemm_tile<T, PHASE, BT, NW>(a, blockIdx.x, lds_raw);
 }
 
 // Wave count of the 256-tile kernels (4: one wave per SIMD with 128x128 each;
@@ -627,6 +811,7 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
 template <typename T, int PHASE>
 void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
     a.n_tiles = n_tiles;
+    if (n_tiles <= 0) return;
     const int grid = n_tiles;
     if (tile == 256) {
         constexpr int NW = MFSDP_WAVES_256;

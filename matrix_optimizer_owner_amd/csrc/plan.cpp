@@ -212,6 +212,13 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             d.n = int32_t(inf.n);
             d.mp = int32_t(align_up(uint64_t(inf.m), kPad));
             d.np = int32_t(align_up(uint64_t(inf.n), kPad));
+            // the kernels address one matrix's Newton-Schulz buffers with
+            // 32-bit signed byte offsets
+            if (uint64_t(d.mp) * uint64_t(d.np) * uint64_t(es) >= (uint64_t(1) << 31)) {
+                delete plan;
+                return fail(MFSDP_ERR_UNSUPPORTED, "entry " + std::to_string(i) +
+                                                       ": padded Newton-Schulz buffer of 2 GiB or more");
+            }
             d.transposed = inf.transposed;
             d.dtype = e.dtype;
             d.lr_scale = inf.lr_scale;

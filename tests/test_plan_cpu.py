@@ -82,6 +82,9 @@ def test_validation_errors():
     assert _status([E(0, 4, 4, dtype=7)]) == 4                       # dtype
     assert _status([E(0, 4, 4, role=9)]) == 4                        # role
     assert _status([E(0, 1 << 23, 1)], pbytes=1 << 30) == 4          # dimension above 2^22
+    # Newton-Schulz buffer (padded, bf16) of 2 GiB: 32768 x 32768
+    assert _status([E(0, 32768, 32768)], pbytes=1 << 31) == 4
+    assert _status([E(0, 32512, 32768)], pbytes=1 << 31) == 0
     assert _status([E(0, 4, 4)], ns_steps=-1) == 1
     assert _status([E(0, 4, 4)], ns_steps=65) == 1
     assert _status([E(0, 4, 4)], ns_precision=2) == 4
