@@ -133,6 +133,36 @@ def cpu_baseline(wl, budget_s: float):
     }
 
 
+# HBM bytes per launch of the dominant kernel, from rocprofv3 counter runs
+# (FETCH_SIZE x2 and WRITE_SIZE x1, the factors a plain device copy of known
+# size reads back), keyed by workload, precision and phase, and valid only
+# for the kernel sources they were taken with.
+TRAFFIC = {
+    # (workload, precision, phase): (sources sha256[:16], fetch bytes, write bytes)
+    ("llama3-8b-owner-share-4L", "bf16", "update"): ("3a292238fad22463", 12129453216, 1861771176),
+}
+TRAFFIC_SOURCES = ("matrix_optimizer_owner_amd/csrc/ns_gemm.hip", "matrix_optimizer_owner_amd/csrc/plan.cpp",
+                   "matrix_optimizer_owner_amd/csrc/layout.h")
+
+
+def sources_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, prec: str, phase: str):
+    rec = TRAFFIC.get((workload, prec, phase))
+    if rec is None or rec[0] != sources_digest():
+        return None
+    return rec[1] + rec[2]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,7 +236,7 @@ def main() -> int:
 
     # per-phase durations from the library's phase-boundary events
     steps_ns = int(hp.get("ns_steps", 5))
-    ph = {"adamw": [], "momentum": [], "gram": [], "poly": [], "update": [], "ns": []}
+    ph = {"adamw": [], "momentum": [], "gram": [], "poly": [], "update": [], "final": [], "ns": []}
     for ev in ev_sets:
         ph["adamw"].append(hip.elapsed_ms(ev[0], ev[1]))
         ph["momentum"].append(hip.elapsed_ms(ev[1], ev[2]))
@@ -215,7 +245,8 @@ def main() -> int:
         for k in range(1, steps_ns + 1):
             ph["gram"].append(hip.elapsed_ms(ev[3 * k - 1], ev[3 * k]))
             ph["poly"].append(hip.elapsed_ms(ev[3 * k], ev[3 * k + 1]))
-            ph["update"].append(hip.elapsed_ms(ev[3 * k + 1], ev[3 * k + 2]))
+            # the last iteration's update kernel also writes the parameters
+            ph["final" if k == steps_ns else "update"].append(hip.elapsed_ms(ev[3 * k + 1], ev[3 * k + 2]))
     for ev in ev_sets:
         hip.destroy(ev)
 
@@ -226,7 +257,7 @@ def main() -> int:
     gram_f = sum(2.0 * min(s.rows, s.cols) ** 2 * max(s.rows, s.cols) for s in specs)
     poly_f = sum(2.0 * min(s.rows, s.cols) ** 3 for s in specs)
     upd_f = gram_f
-    per_launch = {"gram": gram_f, "poly": poly_f, "update": upd_f}
+    per_launch = {"gram": gram_f, "poly": poly_f, "update": upd_f, "final": upd_f}
     tot = {k: sum(ph[k]) for k in per_launch}
     dom = max(tot, key=tot.get) if steps_ns else None
     peak = PEAK_TFLOPS[prec]
@@ -243,8 +274,8 @@ def main() -> int:
         avg = mean(ph[dom])
         ach = per_launch[dom] / (avg * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": None,
-                    "kernel": f"k_ns_gemm ({dom})", "avg_launch_ms": round(avg, 4),
+                    "frac": round(ach / peak, 4), "traffic": measured_traffic(wl.name, prec, dom),
+                    "kernel": f"k_ns_gemm ({dom} phase)", "avg_launch_ms": round(avg, 4),
                     "algorithmic_flop_per_launch": per_launch[dom]}
 
     out = {
@@ -269,7 +300,7 @@ def main() -> int:
         "step_tflops_nominal": round(nominal / (ms * 1e-3) / 1e12, 2),
         "phases_ms": {"adamw": round(adam_ms, 4), "momentum_norm": round(mom_ms, 4), "ns_total": round(ns_ms, 4),
                       "gram_avg": round(mean(ph["gram"]), 4), "poly_avg": round(mean(ph["poly"]), 4),
-                      "update_avg": round(mean(ph["update"]), 4)},
+                      "update_avg": round(mean(ph["update"]), 4), "final_update": round(mean(ph["final"]), 4)},
         "elementwise": {"momentum_gbs": round(k1_bytes / (mom_ms * 1e-3) / 1e9, 1) if mom_ms else None,
                         "momentum_frac_hbm": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if mom_ms else None,
                         "momentum_bytes_per_elem": 12 if prec == "bf16" else 16,
