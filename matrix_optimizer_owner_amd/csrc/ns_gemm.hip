@@ -376,6 +376,57 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     }
 }
 
+// Update epilogue, X'^T = (a X + B X)^T [* s on a first iteration], through
+// LDS: in two passes over halves of the tile's X'^T rows (its columns), the
+// waves owning that half write their fp32 accumulators into LDS in X'^T
+// order (16-byte chunks of a row XOR-swizzled by the row), then the block
+// walks the half row by row: each lane reads 4 accumulators from LDS and the
+// 4 matching X^T elements from HBM, and stores 4 X'^T elements, so every
+// global access of a wave covers whole 512-byte (bf16) rows.
+template <typename T, int BT, int NW>
+__device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                                const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm,
+                                                int wn, int frow, int fhalf, float s1, const T* XTin, T* XTout,
+                                                uint8_t* lds_raw) {
+    using S = Shape<BT, NW>;
+    constexpr int HB = BT / 2;   // X'^T rows per pass
+    constexpr int NCH = BT / 4;  // 16-byte chunks (4 fp32) per staged row
+    static_assert(NCH >= 32, "swizzle range");
+    float* st = reinterpret_cast<float*>(lds_raw);
+    const int64_t mp = d.mp;
+    __syncthreads();  // every wave is done with the operand buffers
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (wn / (S::WC / 2) == h) {
+#pragma unroll
+            for (int mi = 0; mi < S::MM; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < S::MN; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int rl = wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;  // local m index, 4 consecutive
+                        const int cl = wn * S::WTN + ni * 32 + frow - h * HB;      // staged row (local n index)
+                        const int ch = (rl >> 2) ^ (cl & 31);
+                        *reinterpret_cast<float4*>(st + cl * BT + ch * 4) =
+                            make_float4(acc[mi][ni][q * 4], acc[mi][ni][q * 4 + 1], acc[mi][ni][q * 4 + 2],
+                                        acc[mi][ni][q * 4 + 3]);
+                    }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = threadIdx.x; k < HB * NCH; k += S::kThreads) {
+            const int R = k / NCH, c = k % NCH;
+            const float4 v = *reinterpret_cast<const float4*>(st + R * BT + ((c ^ (R & 31)) * 4));
+            const int64_t gi = int64_t(col0 + h * HB + R) * mp + row0 + c * 4;
+            const typename Vec4<T>::raw xv = Vec4<T>::load(XTin + gi);
+            const float o[4] = {(a.ca * Vec4<T>::get(xv, 0) + v.x) * s1, (a.ca * Vec4<T>::get(xv, 1) + v.y) * s1,
+                                (a.ca * Vec4<T>::get(xv, 2) + v.z) * s1, (a.ca * Vec4<T>::get(xv, 3) + v.w) * s1};
+            Vec4<T>::store(XTout + gi, o);
+        }
+        __syncthreads();  // the staging area is free for the next pass
+    }
+}
+
 // Scheduling groups for one stage of the main loop (bf16), in program order:
 // the stage's direct-to-LDS loads and the previous stage's deferred last
 // sub-step of MFMAs, interleaved with sub-step 1's fragment reads; then for
@@ -545,6 +596,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(P)), 0, uni(bytesP), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rsQ =
         __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(Q)), 0, uni(bytesQ), kRsrcWord3);
+    const int KT = K * int(sizeof(T)) / KSB;   // stages along the contraction index
     auto issue = [&](int kt, int buf) {
         const int kp = kt * stepP, kq = kt * stepQ;
 #pragma unroll
@@ -608,7 +660,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[i][jj], af[i], bf[jj]);
     };
 
-    const int KT = K * int(sizeof(T)) / KSB;   // stages along the contraction index
     if constexpr (!PingPong<T, PHASE, BT, NW>::value) {
         // Ring of NBUF stage buffers: stage t lives in buffer t % NBUF and its
         // loads are issued NBUF - 1 stages ahead, into the buffer the previous
@@ -724,31 +775,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         final_update<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
                                 reinterpret_cast<float*>(lds_raw));
         return;
+    } else if constexpr (PHASE == kUpdate) {
+        update_epilogue<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
+                                   reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0])), lds_raw);
+        return;
     } else {
+        // Gram / polynomial: the tile and (off the diagonal) its mirror
         const bool diag = tile.ti == tile.tj;
-        T* out;
-        int ldo;
-        if (PHASE == kGram) {
-            out = reinterpret_cast<T*>(a.ws + d.a_off);
-            ldo = mp;
-        } else if (PHASE == kPoly) {
-            out = reinterpret_cast<T*>(a.ws + d.b_off);
-            ldo = mp;
-        } else {
-            out = reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0]));
-            ldo = mp;
-        }
-        // Epilogue operand, read one MFMA row block ahead along a transposed
-        // layout, where the 4 rows of a lane are 4 consecutive elements: A
-        // itself for the polynomial (A is symmetric), X^T for the update.
-        const T* E = PHASE == kPoly ? reinterpret_cast<const T*>(a.ws + d.a_off) : XTin;
+        T* out = reinterpret_cast<T*>(a.ws + (PHASE == kGram ? d.a_off : d.b_off));
+        const int ldo = mp;
+        // Polynomial epilogue operand A, read one MFMA row block ahead along
+        // its transposed layout (A is symmetric), where the 4 rows of a lane
+        // are 4 consecutive elements.
+        const T* E = reinterpret_cast<const T*>(a.ws + d.a_off);
         auto eaddr = [&](int mi, int ni, int q) -> const T* {
             const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
             const int c = col0 + wn * S::WTN + ni * 32 + frow;
             return E + int64_t(c) * mp + rb;
         };
         typename Vec4<T>::raw ev[2][MN][4];
-        if (PHASE != kGram) {
+        if (PHASE == kPoly) {
 #pragma unroll
             for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
@@ -756,7 +802,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         }
 #pragma unroll
         for (int mi = 0; mi < MM; ++mi) {
-            if (PHASE != kGram && mi + 1 < MM) {
+            if (PHASE == kPoly && mi + 1 < MM) {
 #pragma unroll
                 for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
@@ -770,22 +816,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     const int c = col0 + wn * S::WTN + ni * 32 + frow;
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = acc[mi][ni][q * 4 + e];
-                    if (PHASE == kUpdate) {
-                        // X'^T: the 4 rows of this lane are consecutive in column c of X'^T
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (a.ca * Vec4<T>::get(ev[mi & 1][ni][q], e) + v[e]) * s1;
-                        Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
-                        continue;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            v[e] = PHASE == kGram ? v[e] * (s1 * s1)
-                                                  : a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * v[e];
-                        // mirror tile: the 4 rows of this lane are consecutive in column-major
-                        if (!diag) Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
-                        quad_transpose(v, j);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = PHASE == kGram ? acc[mi][ni][q * 4 + e] * (s1 * s1)
+                                              : a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * acc[mi][ni][q * 4 + e];
+                    // mirror tile: the 4 rows of this lane are consecutive in column-major
+                    if (!diag) Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
+                    quad_transpose(v, j);
                     Vec4<T>::store(out + int64_t(rb + j) * ldo + (c - j), v);
                 }
         }
