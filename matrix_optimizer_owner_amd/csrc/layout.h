@@ -6,9 +6,10 @@
 //                 MatDesc[n_mat], k1_begin[n_mat+1], Tile gram[], Tile poly[],
 //                 Tile upd[], TailDesc[n_tail], tail_begin[n_tail+1]
 //   [s]         float[n_mat]: 1/(||U||_F + eps) per Muon matrix
-//   [partials]  float[n_k1_blocks]: sum of u^2 over one 64x64 tile
+//   [partials]  float[n_k1_blocks]: sum of u^2 over one momentum-kernel tile
 //   per matrix: XT0 and XT1 (np x mp, ping-pong), A and B (mp x mp) in the
-//               Newton-Schulz storage type (bf16 or fp32), row-major.
+//               Newton-Schulz storage type (bf16 or fp32), row-major with
+//               row pitch ld = mp + kLdPad elements.
 //
 // Orientation: every Muon matrix is handled as X (m x n, m <= n).  A tall
 // matrix (rows > cols) is stored transposed.  m and n are padded to
@@ -27,6 +28,13 @@ constexpr int kTileSmall = 128;    // output tile edges of the contraction kerne
 constexpr int kTileLarge = 256;
 constexpr int kLargeTileMin = 512; // a phase uses 256-tiles when it has at least this many
 constexpr int kK1Tile = 128;       // tile edge of the momentum kernel
+// Row pitch pad (elements) of the Newton-Schulz buffers beyond mp.  Pads of
+// 64 and 128 elements (against the power-of-two pitch of most shapes)
+// measured no faster on the Llama-3-8B share; unaligned pads were slower.
+#ifndef MFSDP_LDPAD
+#define MFSDP_LDPAD 0
+#endif
+constexpr int kLdPad = MFSDP_LDPAD;
 constexpr int kTailChunk = 2048;   // elements per AdamW block
 constexpr uint64_t kAlign = 256;
 
@@ -35,10 +43,10 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 struct MatDesc {
     uint64_t param_off;    // bytes into params and grads
     uint64_t mom_off;      // bytes into state (fp32 momentum, rows x cols)
-    uint64_t x_off[2];     // bytes into workspace: X^T ping-pong (np x mp, row-major)
-    uint64_t pad_off;      // unused (keeps the descriptor 8-byte fields in place)
-    uint64_t a_off;        // bytes into workspace: A  (mp x mp)
-    uint64_t b_off;        // bytes into workspace: B  (mp x mp)
+    uint64_t x_off[2];     // bytes into workspace: X^T ping-pong (np rows of ld, row-major)
+    int64_t ld;            // row pitch (elements) of the X^T, A and B buffers: mp + kLdPad
+    uint64_t a_off;        // bytes into workspace: A  (mp rows of ld)
+    uint64_t b_off;        // bytes into workspace: B  (mp rows of ld)
     uint64_t ns_out_off;   // element offset into ns_out (fp32, rows x cols)
     int32_t rows, cols;    // shape as given
     int32_t m, n;          // oriented, m <= n

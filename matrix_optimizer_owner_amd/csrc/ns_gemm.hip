@@ -24,10 +24,12 @@
 // MFMA 32x32 tiles), or 128x128 tiles with 4 waves (two blocks per CU) for
 // phases with too few large tiles to fill the chip.  Operands reach LDS by
 // direct global->LDS loads in 128-byte rows (64 bf16 or 32 fp32 of the
-// contraction index per stage), double-buffered.  Operands that are
-// contiguous along the contraction are read back with 16-byte fragment
-// reads; the Gram's K-major X^T is read back with the transposing LDS read
-// (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
+// contraction index per stage): the bf16 Gram on 256 tiles in two paired
+// stage buffers with a ping-pong schedule, every other phase in split stage
+// rings (3 for P, 2 for Q).  Operands that are contiguous along the
+// contraction are read back with 16-byte fragment reads; the Gram's K-major
+// X^T is read back with the transposing LDS read (ds_read_b64_tr_b16), so X
+// is kept only as X^T.  bf16 uses
 // v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
 // 8-element granule pair).
 #include "device_util.h"
@@ -232,14 +234,6 @@ struct FinalLds {
     static constexpr int FLOATS = HR * PN > BT * PT ? HR * PN : BT * PT;
 };
 
-template <int PHASE, int BT, int NW>
-struct LdsBytes {
-    // main loop: [stage buffer][operand P/Q][KSB-byte rows]; the final
-    // epilogue reuses the same bytes for its O tile
-    static constexpr int main_loop = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>::BYTES;
-    static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
-    static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
-};
 
 // W <- W - lr*wd*W - step*O for n consecutive elements (n <= 4), as one
 // 4-element vector when `vector` (n == 4 and 4-element aligned).
@@ -295,7 +289,7 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     constexpr int HW = S::WTM / 2;  // rows of one wave's block per half
     const bool tr = d.transposed != 0;
     const float step = a.lr * d.lr_scale;
-    const int mp = d.mp;
+    const int64_t ld = d.ld;  // row pitch of X^T
     const int64_t ldw = d.cols;
     const bool vec = (d.cols & 3) == 0;
     uint8_t* Wb = a.params + d.param_off;
@@ -316,7 +310,7 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
                 for (int q = 0; q < 4; ++q) {
                     const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
                     const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                    xv[ni][q] = Vec4<T>::load(XTin + int64_t(c) * mp + rb);
+                    xv[ni][q] = Vec4<T>::load(XTin + int64_t(c) * ld + rb);
                 }
 #pragma unroll
             for (int ni = 0; ni < S::MN; ++ni)
@@ -393,7 +387,7 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
     constexpr int NCH = BT / 4;  // 16-byte chunks (4 fp32) per staged row
     static_assert(NCH >= 32, "swizzle range");
     float* st = reinterpret_cast<float*>(lds_raw);
-    const int64_t mp = d.mp;
+    const int64_t ld = d.ld;  // row pitch of X^T and X'^T
     __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -417,7 +411,7 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
         for (int k = threadIdx.x; k < HB * NCH; k += S::kThreads) {
             const int R = k / NCH, c = k % NCH;
             const float4 v = *reinterpret_cast<const float4*>(st + R * BT + ((c ^ (R & 31)) * 4));
-            const int64_t gi = int64_t(col0 + h * HB + R) * mp + row0 + c * 4;
+            const int64_t gi = int64_t(col0 + h * HB + R) * ld + row0 + c * 4;
             const typename Vec4<T>::raw xv = Vec4<T>::load(XTin + gi);
             const float o[4] = {(a.ca * Vec4<T>::get(xv, 0) + v.x) * s1, (a.ca * Vec4<T>::get(xv, 1) + v.y) * s1,
                                 (a.ca * Vec4<T>::get(xv, 2) + v.z) * s1, (a.ca * Vec4<T>::get(xv, 3) + v.w) * s1};
@@ -472,8 +466,21 @@ __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Block barrier between main-loop stages.  __syncthreads() is a workgroup
+// release fence and waits for every outstanding vector-memory load
+// (vmcnt(0)), which would also wait for look-ahead loads of later stages;
+// the loads a stage needs are waited for explicitly (wait_vmcnt) before it,
+// so this barrier only waits for the wave's LDS reads (the slot they read
+// may be refilled after it).
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 #ifndef MFSDP_PINGPONG
 #define MFSDP_PINGPONG 1
+#endif
+#ifndef MFSDP_RING32
+#define MFSDP_RING32 1
 #endif
 #ifndef MFSDP_PP_BURST
 #define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
@@ -483,10 +490,35 @@ __device__ __forceinline__ void phase_barrier() {
 // 7% faster (its transposing fragment reads are twice as many instructions,
 // which batch better than they interleave) and the row-major phases 5%
 // slower; half-stage bursts were slower for all three.
+// Split 3/2 stage rings (P two stages ahead) serve every phase that does not
+// run the ping-pong, with 128-byte stages; they take 5 operand stages of LDS
+// (160 KB for 256 tiles, 80 KB for 128 tiles).  On the Llama-3-8B share they
+// measured about 1% faster than two paired buffers; look-ahead beyond that
+// (64-byte stages in 3 to 5 buffers, or an L2 prefetch of later stages) was
+// slower: the stage time is set by the volume of loads per CU rather than by
+// their latency.
+template <typename T, int PHASE, int BT, int NW>
+struct PingPong;
+template <typename T, int PHASE, int BT, int NW>
+struct Ring32 {
+    static constexpr bool value = MFSDP_RING32 && !PingPong<T, PHASE, BT, NW>::value && PipeFor<BT>::KSB == 128 &&
+                                  PipeFor<BT>::NBUF == 2;
+};
 template <typename T, int PHASE, int BT, int NW>
 struct PingPong {
     static constexpr bool value = MFSDP_PINGPONG && sizeof(T) == 2 && PHASE == kGram && BT == 256 && NW == 8 &&
                                   PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
+};
+
+// LDS of the block: the main loop's operand stages (the split rings take 5
+// operand stages, the paired buffers 2 * NBUF); the epilogues reuse the same
+// bytes (the final update slightly more of them for its O tile).
+template <typename T, int PHASE, int BT, int NW>
+struct LdsBytes {
+    using PP = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>;
+    static constexpr int main_loop = Ring32<T, PHASE, BT, NW>::value ? 5 * PP::OPB : PP::BYTES;
+    static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
+    static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
 };
 
 // C = P Q^T over one BT x BT output tile, then the phase's epilogue.
@@ -501,7 +533,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
-    const int mp = d.mp, np = d.np;
+    const int mp = d.mp, np = d.np, ld = int(d.ld);
     const int row0 = int(tile.ti) * BT, col0 = int(tile.tj) * BT;
     const T* XTin = reinterpret_cast<const T*>(a.ws + (a.x_in ? d.x_off[1] : d.x_off[0]));
 
@@ -510,16 +542,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     int ldp, ldq, K;
     if (PHASE == kGram) {
         P = Q = XTin;
-        ldp = ldq = mp;
+        ldp = ldq = ld;
         K = np;
     } else if (PHASE == kPoly) {
         P = Q = reinterpret_cast<const T*>(a.ws + d.a_off);
-        ldp = ldq = mp;
+        ldp = ldq = ld;
         K = mp;
     } else {
         P = reinterpret_cast<const T*>(a.ws + d.b_off);
         Q = XTin;
-        ldp = ldq = mp;
+        ldp = ldq = ld;
         K = mp;
     }
 
@@ -587,8 +619,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         }
     }
     // bytes of each operand's matrix buffer, and between consecutive stages
-    const int bytesP = (PHASE == kGram ? np : mp) * mp * ES;
-    const int bytesQ = (PHASE == kPoly ? mp : np) * mp * ES;
+    const int bytesP = (PHASE == kGram ? np : mp) * ld * ES;
+    const int bytesQ = (PHASE == kPoly ? mp : np) * ld * ES;
     const int stepP = uni(KM ? KST * ldp * ES : KSB);
     const int stepQ = uni(KM ? KST * ldq * ES : KSB);
     // (the resources and wave offsets must live in scalar registers)
@@ -597,6 +629,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     const __amdgpu_buffer_rsrc_t rsQ =
         __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(Q)), 0, uni(bytesQ), kRsrcWord3);
     const int KT = K * int(sizeof(T)) / KSB;   // stages along the contraction index
+    auto issue_one = [&](const __amdgpu_buffer_rsrc_t& rs, const int (&u)[LP], int step, int kt, int off) {
+#pragma unroll
+        for (int i = 0; i < LP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]), 16, int(voff), u[i] + kt * step,
+                0, 0);
+    };
     auto issue = [&](int kt, int buf) {
         const int kp = kt * stepP, kq = kt * stepQ;
 #pragma unroll
@@ -612,8 +651,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     // K-major tile: bf16, two transposing reads (k0..k0+3 and k0+4..k0+7);
     // fp32, four scalar reads.  Lane l needs column c + l%32 and the
     // contraction indices of its MFMA half l/32.
-    auto kmajor_frag = [&](int b, int op, int c, int kk) -> u32x4_t {
-        const uint8_t* base = lds_raw + (2 * b + op) * OPB;
+    auto kmajor_frag = [&](int off, int c, int kk) -> u32x4_t {
+        const uint8_t* base = lds_raw + off;
         if constexpr (sizeof(T) == 2) {
             const int g16 = lane >> 4, sl = lane & 15;
             const int col = c + 16 * (g16 & 1) + 4 * (sl & 3);   // this lane's source column
@@ -636,22 +675,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             return out;
         }
     };
-    auto rowmajor_frag = [&](int b, int op, int r, int kk) -> u32x4_t {
-        const uint8_t* base = lds_raw + (2 * b + op) * OPB;
+    auto rowmajor_frag = [&](int off, int r, int kk) -> u32x4_t {
+        const uint8_t* base = lds_raw + off;
         return *reinterpret_cast<const u32x4_t*>(base + r * KSB + swz_r<GR>(r, 2 * kk + fhalf) * 16);
     };
-    auto frags = [&](int b, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
+    // fragments of sub-step kk from the P and Q stage slots at byte offsets oP, oQ
+    auto frags2 = [&](int oP, int oQ, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
         if constexpr (KM) {
 #pragma unroll
-            for (int i = 0; i < MM; ++i) af[i] = kmajor_frag(b, 0, wm * S::WTM + i * 32, kk);
+            for (int i = 0; i < MM; ++i) af[i] = kmajor_frag(oP, wm * S::WTM + i * 32, kk);
 #pragma unroll
-            for (int jj = 0; jj < MN; ++jj) bf[jj] = kmajor_frag(b, 1, wn * S::WTN + jj * 32, kk);
+            for (int jj = 0; jj < MN; ++jj) bf[jj] = kmajor_frag(oQ, wn * S::WTN + jj * 32, kk);
         } else {
 #pragma unroll
-            for (int i = 0; i < MM; ++i) af[i] = rowmajor_frag(b, 0, wm * S::WTM + i * 32 + frow, kk);
+            for (int i = 0; i < MM; ++i) af[i] = rowmajor_frag(oP, wm * S::WTM + i * 32 + frow, kk);
 #pragma unroll
-            for (int jj = 0; jj < MN; ++jj) bf[jj] = rowmajor_frag(b, 1, wn * S::WTN + jj * 32 + frow, kk);
+            for (int jj = 0; jj < MN; ++jj) bf[jj] = rowmajor_frag(oQ, wn * S::WTN + jj * 32 + frow, kk);
         }
+    };
+    // stage buffer b of the paired layout: P at (2b) * OPB, Q at (2b + 1) * OPB
+    auto frags = [&](int b, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
+        frags2(2 * b * OPB, (2 * b + 1) * OPB, kk, af, bf);
     };
     auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
 #pragma unroll
@@ -660,7 +704,54 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[i][jj], af[i], bf[jj]);
     };
 
-    if constexpr (!PingPong<T, PHASE, BT, NW>::value) {
+    if constexpr (Ring32<T, PHASE, BT, NW>::value) {
+        // Split rings: P's stage slots form a ring of 3 (byte offsets 0, OPB,
+        // 2*OPB), Q's a ring of 2 (3*OPB, 4*OPB).  During stage t the block
+        // loads Q of stage t + 1 and then P of stage t + 2, each into the slot
+        // stage t - 1 has just released (every wave passed the barrier that
+        // ended it).  At the end of stage t a wave waits for all but its LP
+        // most recent loads (loads complete in issue order), i.e. for Q of
+        // t + 1 and, one stage older, P of t + 1: only half of the data has a
+        // single stage to arrive.  Past the end the look-ahead re-loads the
+        // last stage into released slots no later stage reads.  Inside a
+        // stage, the sub-step pipeline of the two-buffer schedule.
+        issue_one(rsP, uP, stepP, 0, 0);
+        issue_one(rsQ, uQ, stepQ, 0, 3 * OPB);
+        issue_one(rsP, uP, stepP, 1 < KT ? 1 : KT - 1, OPB);
+        wait_vmcnt<LP>();
+        stage_barrier();
+        u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
+#pragma unroll
+        for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
+        frags2(0, 3 * OPB, 0, fa0, fb0);
+        int sp = 0, sq = 0;  // P and Q slots of stage kt
+        for (int kt = 0; kt < KT; ++kt) {
+            const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
+            issue_one(rsQ, uQ, stepQ, kt + 1 < KT ? kt + 1 : KT - 1, (3 + (sq ^ 1)) * OPB);
+            issue_one(rsP, uP, stepP, kt + 2 < KT ? kt + 2 : KT - 1, sp2 * OPB);
+            mfmas(fa1, fb1);  // last sub-step of the previous stage (zeros on the first)
+#pragma unroll
+            for (int u = 1; u < SUBS; ++u) {
+                if (u & 1) {
+                    frags2(sp * OPB, (3 + sq) * OPB, u, fa1, fb1);
+                    mfmas(fa0, fb0);  // sub-step u - 1
+                } else {
+                    frags2(sp * OPB, (3 + sq) * OPB, u, fa0, fb0);
+                    mfmas(fa1, fb1);
+                }
+            }
+            if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), 2 * LP, SUBS>();
+            wait_vmcnt<LP>();
+            stage_barrier();
+            sp = sp == 2 ? 0 : sp + 1;
+            sq ^= 1;
+            frags2(sp * OPB, (3 + sq) * OPB, 0, fa0, fb0);  // next stage's first fragments
+        }
+        mfmas(fa1, fb1);  // last sub-step of the last stage
+        wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
+    } else if constexpr (!PingPong<T, PHASE, BT, NW>::value) {
         // Ring of NBUF stage buffers: stage t lives in buffer t % NBUF and its
         // loads are issued NBUF - 1 stages ahead, into the buffer the previous
         // stage has just released (every wave passed the barrier that ended it).
@@ -678,7 +769,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     #pragma unroll
         for (int t = 0; t < D; ++t) issue(t < KT ? t : KT - 1, t);
         wait_vmcnt<VM_STAGE * (D - 1)>();
-        __syncthreads();
+        stage_barrier();
 
         u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
     #pragma unroll
@@ -703,7 +794,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             }
             if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), VM_STAGE, SUBS>();
             wait_vmcnt<VM_STAGE * (D - 1)>();
-            __syncthreads();
+            stage_barrier();
             buf = buf + 1 == NBUF ? 0 : buf + 1;
             lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
             frags(buf, 0, fa0, fb0);  // next stage's first fragments
@@ -783,7 +874,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         // Gram / polynomial: the tile and (off the diagonal) its mirror
         const bool diag = tile.ti == tile.tj;
         T* out = reinterpret_cast<T*>(a.ws + (PHASE == kGram ? d.a_off : d.b_off));
-        const int ldo = mp;
+        const int ldo = ld;
         // Polynomial epilogue operand A, read one MFMA row block ahead along
         // its transposed layout (A is symmetric), where the 4 rows of a lane
         // are 4 consecutive elements.
@@ -791,7 +882,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         auto eaddr = [&](int mi, int ni, int q) -> const T* {
             const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
             const int c = col0 + wn * S::WTN + ni * 32 + frow;
-            return E + int64_t(c) * mp + rb;
+            return E + int64_t(c) * ld + rb;
         };
         typename Vec4<T>::raw ev[2][MN][4];
         if (PHASE == kPoly) {
@@ -834,7 +925,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 // share.
 template <typename T, int PHASE, int BT, int NW>
 __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<PHASE, BT, NW>::value];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<T, PHASE, BT, NW>::value];
     gemm_tile<T, PHASE, BT, NW>(a, blockIdx.x, lds_raw);
 }
 

@@ -214,7 +214,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             d.np = int32_t(align_up(uint64_t(inf.n), kPad));
             // the kernels address one matrix's Newton-Schulz buffers with
             // 32-bit signed byte offsets
-            if (uint64_t(d.mp) * uint64_t(d.np) * uint64_t(es) >= (uint64_t(1) << 31)) {
+            d.ld = d.mp + kLdPad;
+            if (uint64_t(d.ld) * uint64_t(d.np) * uint64_t(es) >= (uint64_t(1) << 31)) {
                 delete plan;
                 return fail(MFSDP_ERR_UNSUPPORTED, "entry " + std::to_string(i) +
                                                        ": padded Newton-Schulz buffer of 2 GiB or more");
@@ -330,8 +331,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         w.off_partials = section(uint64_t(k1_begin.back()) * sizeof(float));
         for (size_t k = 0; k < mats.size(); ++k) {
             MatDesc& d = mats[k];
-            const uint64_t xbytes = uint64_t(d.mp) * uint64_t(d.np) * uint64_t(es);
-            const uint64_t abytes = uint64_t(d.mp) * uint64_t(d.mp) * uint64_t(es);
+            const uint64_t xbytes = uint64_t(d.ld) * uint64_t(d.np) * uint64_t(es);
+            const uint64_t abytes = uint64_t(d.ld) * uint64_t(d.mp) * uint64_t(es);
             d.x_off[0] = section(xbytes);
             d.x_off[1] = section(xbytes);
             d.a_off = section(abytes);

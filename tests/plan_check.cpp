@@ -85,7 +85,8 @@ int main() {
     regs.push_back({w.off_partials, uint64_t(w.n_k1_blocks) * 4});
     for (int k = 0; k < w.n_mat; ++k) {
         const MatDesc& d = mats[k];
-        const uint64_t xb = uint64_t(d.mp) * d.np * es_ns, ab = uint64_t(d.mp) * d.mp * es_ns;
+        CHECK(d.ld == d.mp + kLdPad && (d.ld * es_ns) % 128 == 0, "matrix %d row pitch", k);
+        const uint64_t xb = uint64_t(d.ld) * d.np * es_ns, ab = uint64_t(d.ld) * d.mp * es_ns;
         regs.push_back({d.x_off[0], xb});
         regs.push_back({d.x_off[1], xb});
         regs.push_back({d.a_off, ab});
