@@ -237,6 +237,7 @@ def main() -> int:
     # per-phase durations from the library's phase-boundary events
     steps_ns = int(hp.get("ns_steps", 5))
     ph = {"adamw": [], "momentum": [], "gram": [], "poly": [], "update": [], "final": [], "ns": []}
+    step_ms = [hip.elapsed_ms(ev[0], ev[n_ev - 1]) for ev in ev_sets]
     for ev in ev_sets:
         ph["adamw"].append(hip.elapsed_ms(ev[0], ev[1]))
         ph["momentum"].append(hip.elapsed_ms(ev[1], ev[2]))
@@ -269,6 +270,35 @@ def main() -> int:
     mom_ms = mean(ph["momentum"])
     adam_ms = mean(ph["adamw"])
 
+    # executed NS FLOPs: the Gram and the polynomial compute upper tiles only
+    # (256-tile edge when a phase has at least 512 of them, else 128, as the
+    # planner chooses), on the padded shapes
+    def executed_ns_flops():
+        def pad(x):
+            return (x + 255) // 256 * 256
+        dims = [(pad(min(s.rows, s.cols)), pad(max(s.rows, s.cols))) for s in specs]
+        def edge(count256):
+            return 256 if count256 >= 512 else 128
+        g_t = edge(sum((m // 256) * (m // 256 + 1) // 2 for m, _ in dims))
+        u_t = edge(sum((m // 256) * (n // 256) for m, n in dims))
+        gram = sum((m // g_t) * (m // g_t + 1) // 2 * g_t * g_t * 2.0 * n for m, n in dims)
+        poly = sum((m // g_t) * (m // g_t + 1) // 2 * g_t * g_t * 2.0 * m for m, n in dims)
+        upd = sum(2.0 * m * m * n for m, n in dims)
+        return steps_ns * (gram + poly + upd)
+
+    # device-copy ceiling of this GPU, measured live (1 GiB read + 1 GiB written)
+    cbuf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    csrc, cdst = cbuf[: 1 << 30], cbuf[1 << 30:]
+    for _ in range(2):
+        cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) * 5 / (time.perf_counter() - c0) / 1e9
+    del cbuf, csrc, cdst
+
     roofline = None
     if dom:
         avg = mean(ph[dom])
@@ -294,9 +324,13 @@ def main() -> int:
         "config": {"workload": wl.name, "muon_matrices": len(specs), "muon_elements": muon_el,
                    "tail_tensors": sum(1 for s in wl.specs if s not in specs and s.numel > 0),
                    "tail_elements": tail_el, "ns_steps": steps_ns, "parallelism": "single GPU owner"},
+        "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "step_ms_p90": round(sorted(step_ms)[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4),
+        "step_ms_all": [round(x, 4) for x in step_ms],
         "matrices_per_s": round(len(specs) / (ms * 1e-3), 2),
         "ns_tflops_nominal": round(nominal / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "ns_frac_peak": round(nominal / (ns_ms * 1e-3) / 1e12 / peak, 4) if ns_ms else None,
+        "ns_tflops_executed": round(executed_ns_flops() / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "step_tflops_nominal": round(nominal / (ms * 1e-3) / 1e12, 2),
         "phases_ms": {"adamw": round(adam_ms, 4), "momentum_norm": round(mom_ms, 4), "ns_total": round(ns_ms, 4),
                       "gram_avg": round(mean(ph["gram"]), 4), "poly_avg": round(mean(ph["poly"]), 4),
@@ -304,6 +338,8 @@ def main() -> int:
         "elementwise": {"momentum_gbs": round(k1_bytes / (mom_ms * 1e-3) / 1e9, 1) if mom_ms else None,
                         "momentum_frac_hbm": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if mom_ms else None,
                         "momentum_bytes_per_elem": 12 if prec == "bf16" else 16,
+                        "copy_ceiling_gbs": round(copy_gbs, 1),
+                        "momentum_frac_copy_ceiling": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / copy_gbs, 4) if mom_ms else None,
                         "adamw_gbs": round(28 * tail_el / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},
         "roofline": roofline,
         "cpu_baseline": None,
