@@ -32,6 +32,8 @@
 // is kept only as X^T.  bf16 uses
 // v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
 // 8-element granule pair).
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -299,6 +301,33 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        // The block walks the half tile in W's memory order, 4 elements per
+        // chunk; a thread owns chunks threadIdx.x + j * kThreads and issues the
+        // W loads of a batch of chunks (8 for bf16, 4 for fp32) before it
+        // consumes any: one W round trip per batch.
+        constexpr int CHUNKS = L::HR * BT / 4;
+        constexpr int NPT = CHUNKS / S::kThreads;
+        static_assert(CHUNKS % S::kThreads == 0, "walk");
+        auto chunk = [&](int j, int& lofs, int64_t& widx, int& n_ok) {
+            const int k = threadIdx.x + j * S::kThreads;
+            if (tr) {
+                const int lc = k / (L::HR / 4);
+                const int lr = (k % (L::HR / 4)) * 4;
+                lofs = lc * L::PT + lr;
+                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;  // tile row -> W column
+                const int gc = col0 + lc;                                     // tile column -> W row
+                widx = int64_t(gc) * ldw + gr;
+                n_ok = gc < w_rows ? min(4, w_cols - gr) : 0;
+            } else {
+                const int lr = k / (BT / 4);
+                const int lc = (k % (BT / 4)) * 4;
+                lofs = lr * L::PN + lc;
+                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;
+                const int gc = col0 + lc;
+                widx = int64_t(gr) * ldw + gc;
+                n_ok = gr < w_rows ? min(4, w_cols - gc) : 0;
+            }
+        };
         // 1) O for this half into LDS, in W's orientation
 #pragma unroll
         for (int mh = 0; mh < S::MM / 2; ++mh) {
@@ -332,40 +361,47 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
                 }
         }
         __syncthreads();
-        // 2) walk the half tile in W's memory order, 4 elements per step
-        constexpr int CHUNKS = L::HR * BT / 4;
-#pragma unroll 2
-        for (int k = threadIdx.x; k < CHUNKS; k += S::kThreads) {
-            float o[4];
-            int64_t widx;
-            int n_ok;
-            if (tr) {
-                const int lc = k / (L::HR / 4);
-                const int lr = (k % (L::HR / 4)) * 4;
-                const float4 v = *reinterpret_cast<const float4*>(olds + lc * L::PT + lr);
-                o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;  // tile row -> W column
-                const int gc = col0 + lc;                                     // tile column -> W row
-                widx = int64_t(gc) * ldw + gr;
-                n_ok = gc < w_rows ? min(4, w_cols - gr) : 0;
-            } else {
-                const int lr = k / (BT / 4);
-                const int lc = (k % (BT / 4)) * 4;
-                const float4 v = *reinterpret_cast<const float4*>(olds + lr * L::PN + lc);
-                o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;
-                const int gc = col0 + lc;
-                widx = int64_t(gr) * ldw + gc;
-                n_ok = gr < w_rows ? min(4, w_cols - gc) : 0;
+        // 2) walk the half tile in W's memory order (see above)
+        auto walk = [&](auto* W) {
+            using WT_ = typename std::remove_pointer<decltype(W)>::type;
+            constexpr int NB0 = sizeof(WT_) == 2 ? 8 : 4;  // W loads in flight
+            constexpr int NB = NPT < NB0 ? NPT : NB0;
+            static_assert(NPT % NB == 0, "batches");
+#pragma unroll
+            for (int j0 = 0; j0 < NPT; j0 += NB) {
+                typename Vec4<WT_>::raw raw[NB];
+                int64_t widx[NB];
+                int n_ok[NB], lofs[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    chunk(j0 + b, lofs[b], widx[b], n_ok[b]);
+                    if (vec && n_ok[b] == 4) raw[b] = Vec4<WT_>::load(W + widx[b]);
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (n_ok[b] <= 0) continue;
+                    const float4 v = *reinterpret_cast<const float4*>(olds + lofs[b]);
+                    const float o[4] = {v.x, v.y, v.z, v.w};
+                    float* op = O ? O + widx[b] : nullptr;
+                    if (vec && n_ok[b] == 4) {
+                        float r[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = Vec4<WT_>::get(raw[b], e);
+                            r[e] = __builtin_fmaf(-step, o[e], __builtin_fmaf(-a.lrwd, x, x));
+                        }
+                        Vec4<WT_>::store(W + widx[b], r);
+                        if (op) *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+                    } else {
+                        w_update4<WT_>(W + widx[b], op, o, a.lrwd, step, n_ok[b], false);
+                    }
+                }
             }
-            if (n_ok <= 0) continue;
-            const bool vector = vec && n_ok == 4;
-            float* op = O ? O + widx : nullptr;
-            if (d.dtype == kBF16)
-                w_update4<uint16_t>(reinterpret_cast<uint16_t*>(Wb) + widx, op, o, a.lrwd, step, n_ok, vector);
-            else
-                w_update4<float>(reinterpret_cast<float*>(Wb) + widx, op, o, a.lrwd, step, n_ok, vector);
-        }
+        };
+        if (d.dtype == kBF16)
+            walk(reinterpret_cast<uint16_t*>(Wb));
+        else
+            walk(reinterpret_cast<float*>(Wb));
         __syncthreads();
     }
 }
