@@ -518,6 +518,7 @@ __device__ __forceinline__ void stage_barrier() {
 #ifndef MFSDP_RING32
 #define MFSDP_RING32 1
 #endif
+
 #ifndef MFSDP_PP_BURST
 #define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
 #endif
@@ -957,8 +958,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 
 // One block per tile: the hardware dispatcher then hands the cost-sorted
 // tile list to CUs as they free up (greedy longest-first).  A persistent grid
-// walking the list with a fixed stride measured slower on the Llama-3-8B
-// share.
+// walking the list with a fixed stride measured no faster on the Llama-3-8B
+// share: stores and loads share the in-order vmcnt counter, so the next
+// tile's first wait for its loads also waits for the previous tile's
+// epilogue stores.
 template <typename T, int PHASE, int BT, int NW>
 __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_raw[LdsBytes<T, PHASE, BT, NW>::value];
