@@ -1,0 +1,92 @@
+"""GPU parity of the option paths and launch shapes the default workloads do
+not reach: Newton-Schulz step counts 0, 1 and 2 (no iteration: the update
+straight from the normalised input; the first iteration also being the
+last), the alternative learning-rate shape scale, plain (non-Nesterov)
+momentum, explicit role overrides, the 256-tile kernels on ragged shapes,
+and bitwise run-to-run determinism."""
+
+import numpy as np
+import pytest
+
+from matrix_optimizer_owner_amd import binding as B
+from matrix_optimizer_owner_amd import workloads as W
+from tests.harness import GpuRun, assert_reports, check_step, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _steps(wl, steps, hp_overrides=None, label=""):
+    run = GpuRun(wl, hp_overrides)
+    try:
+        for t in range(1, steps + 1):
+            say(f"[{label}] step {t}: {wl.name}")
+            run.fill(t, params_too=(t == 1))
+            before = run.host()
+            run.run(t)
+            after = run.host()
+            assert_reports(check_step(run, before, after, t), f"{label} t={t}")
+    finally:
+        run.free()
+
+
+@pytest.mark.parametrize("ns_steps", [0, 1, 2])
+def test_newton_schulz_step_counts(ns_steps):
+    _steps(W.small_ragged(precision=0), 1, {"ns_steps": ns_steps}, label=f"ns{ns_steps}")
+
+
+def test_ns_steps_zero_fp32():
+    _steps(W.small_ragged(precision=1), 1, {"ns_steps": 0}, label="ns0-fp32")
+
+
+def test_shape_scale_mode_1_and_plain_momentum():
+    # two steps, so that the momentum form matters
+    _steps(W.small_ragged(precision=0), 2, {"lr_scale_mode": 1, "nesterov": 0}, label="scale1-plain")
+
+
+def test_role_overrides():
+    sp = [
+        W.TensorSpec("forced_adamw", 96, 160, "f32", role="adamw", grad_std=1e-3),
+        W.TensorSpec("forced_muon", 130, 70, role="muon", grad_std=1e-2),
+        W.TensorSpec("auto_matrix", 64, 300, grad_std=1e-3),
+        W.TensorSpec("auto_vector", 1, 500, "f32", grad_std=1e-3),
+    ]
+    wl = W.Workload("role-overrides", sp, seed=11, hparams=dict(W.MUON_DEFAULTS, ns_precision=0))
+    run = GpuRun(wl)
+    try:
+        assert [run.info[i].role for i in range(4)] == [B.ROLE_ADAMW, B.ROLE_MUON, B.ROLE_MUON, B.ROLE_ADAMW]
+    finally:
+        run.free()
+    _steps(wl, 2, label="roles")
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_ragged_shapes_on_256_tiles(precision, monkeypatch):
+    """Force the 256x256 tile kernels (for bf16: the ping-pong Gram and the
+    split-ring phases with 8 waves) onto shapes that are not multiples of
+    256, so their padding and the final update's bounds are exercised."""
+    monkeypatch.setenv("MFSDP_TILE", "256")
+    _steps(W.small_ragged(precision=precision), 2, label=f"t256-p{precision}")
+
+
+def test_bitwise_deterministic():
+    """Two runs of the same step from the same state give identical bytes
+    (fixed-order Sigma u^2, no float atomics); the second run reuses the
+    descriptors already resident in the workspace."""
+    wl = W.config(1)
+    run = GpuRun(wl)
+    try:
+        run.fill(1, params_too=True)
+        p0, s0 = run.params.clone(), run.state.clone()
+        run.run(1)
+        first = (run.params.clone(), run.state.clone(), run.ns_out.clone())
+        run.params.copy_(p0)
+        run.state.copy_(s0)
+        run.run(1, flags=B.STEP_DESCRIPTORS_RESIDENT)
+        second = (run.params, run.state, run.ns_out)
+        run.torch.cuda.synchronize()
+        for name, x, y in zip(("params", "state", "ns_out"), first, second):
+            same = bool(run.torch.equal(x.view(run.torch.uint8), y.view(run.torch.uint8)))
+            say(f"  {name}: bitwise equal = {same}")
+            assert same, name
+    finally:
+        run.free()
