@@ -29,9 +29,8 @@
 // rings (3 for P, 2 for Q).  Operands that are contiguous along the
 // contraction are read back with 16-byte fragment reads; the Gram's K-major
 // X^T is read back with the transposing LDS read (ds_read_b64_tr_b16), so X
-// is kept only as X^T.  bf16 uses
-// v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
-// 8-element granule pair).
+// is kept only as X^T.  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses
+// v_mfma_f32_32x32x2_f32 (four per 8-element granule pair).
 #include <type_traits>
 
 #include "device_util.h"
@@ -204,11 +203,11 @@ struct Pipe {
     static_assert(NBUF >= 2 && 2 * LP * (NBUF - 2) <= 63, "vmcnt range");
 };
 
-// Stage geometry per tile edge: (KSB, NBUF).  128-byte stages, two buffers
-// (256 tiles: 128 KB; 128 tiles, two blocks per CU: 64 KB each).  On the
-// Llama-3-8B share, 64-byte stages with 3 to 5 buffers (more look-ahead, twice
-// the barriers) measured 16% slower, and the look-ahead depth made no
-// difference: the loop is not bound by load latency.
+// Stage geometry per tile edge: (KSB, NBUF) of the paired layout, where a
+// stage buffer holds both operands (the ping-pong Gram; the split rings use
+// the same 128-byte stages in 5 operand slots).  On the Llama-3-8B share,
+// 64-byte stages with 3 to 5 paired buffers (more look-ahead, twice the
+// barriers) measured 10-20% slower than 128-byte stages.
 #ifndef MFSDP_KSB_256
 #define MFSDP_KSB_256 128
 #endif
@@ -235,7 +234,6 @@ struct FinalLds {
     static constexpr int PT = HR + 4;
     static constexpr int FLOATS = HR * PN > BT * PT ? HR * PN : BT * PT;
 };
-
 
 // W <- W - lr*wd*W - step*O for n consecutive elements (n <= 4), as one
 // 4-element vector when `vector` (n == 4 and 4-element aligned).
@@ -515,36 +513,35 @@ __device__ __forceinline__ void stage_barrier() {
 #ifndef MFSDP_PINGPONG
 #define MFSDP_PINGPONG 1
 #endif
+#ifndef MFSDP_PP_BURST
+#define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
+#endif
 #ifndef MFSDP_RING32
 #define MFSDP_RING32 1
 #endif
 
-#ifndef MFSDP_PP_BURST
-#define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
-#endif
 // The ping-pong schedule serves the bf16 Gram on 256 tiles with 8 waves and
-// 128-byte stages in two buffers.  On the Llama-3-8B share it made the Gram
-// 7% faster (its transposing fragment reads are twice as many instructions,
-// which batch better than they interleave) and the row-major phases 5%
-// slower; half-stage bursts were slower for all three.
-// Split 3/2 stage rings (P two stages ahead) serve every phase that does not
-// run the ping-pong, with 128-byte stages; they take 5 operand stages of LDS
-// (160 KB for 256 tiles, 80 KB for 128 tiles).  On the Llama-3-8B share they
-// measured about 1% faster than two paired buffers; look-ahead beyond that
-// (64-byte stages in 3 to 5 buffers, or an L2 prefetch of later stages) was
-// slower: the stage time is set by the volume of loads per CU rather than by
-// their latency.
-template <typename T, int PHASE, int BT, int NW>
-struct PingPong;
-template <typename T, int PHASE, int BT, int NW>
-struct Ring32 {
-    static constexpr bool value = MFSDP_RING32 && !PingPong<T, PHASE, BT, NW>::value && PipeFor<BT>::KSB == 128 &&
-                                  PipeFor<BT>::NBUF == 2;
-};
+// 128-byte stages in two paired buffers.  On the Llama-3-8B share it made
+// the Gram 2-7% faster (its transposing fragment reads are twice as many
+// instructions, which batch better than they interleave) and the row-major
+// phases slower; half-stage bursts were slower for all three.
 template <typename T, int PHASE, int BT, int NW>
 struct PingPong {
     static constexpr bool value = MFSDP_PINGPONG && sizeof(T) == 2 && PHASE == kGram && BT == 256 && NW == 8 &&
                                   PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
+};
+
+// Split 3/2 stage rings (P loaded two stages ahead) serve every phase that
+// does not run the ping-pong, with 128-byte stages; they take 5 operand
+// stages of LDS (160 KB for 256 tiles, 80 KB for 128 tiles).  On the
+// Llama-3-8B share they measured about 1% faster than two paired buffers;
+// look-ahead beyond that (64-byte stages in 3 to 5 buffers, or an L2
+// prefetch of later stages) was slower: the stage time is set by the volume
+// of loads per CU rather than by their latency.
+template <typename T, int PHASE, int BT, int NW>
+struct Ring32 {
+    static constexpr bool value = MFSDP_RING32 && !PingPong<T, PHASE, BT, NW>::value && PipeFor<BT>::KSB == 128 &&
+                                  PipeFor<BT>::NBUF == 2;
 };
 
 // LDS of the block: the main loop's operand stages (the split rings take 5
