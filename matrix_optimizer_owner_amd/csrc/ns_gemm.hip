@@ -296,6 +296,9 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;
     const int w_rows = d.rows, w_cols = d.cols;
     const int j = frow & 3;
+    // The O tile reuses the operand stages: every wave's last direct-to-LDS
+    // loads (the main loop's look-ahead past the end) must have landed.
+    __syncthreads();
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -409,8 +412,11 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
 // waves owning that half write their fp32 accumulators into LDS in X'^T
 // order (16-byte chunks of a row XOR-swizzled by the row), then the block
 // walks the half row by row: each lane reads 4 accumulators from LDS and the
-// 4 matching X^T elements from HBM, and stores 4 X'^T elements, so every
-// global access of a wave covers whole 512-byte (bf16) rows.
+// 4 matching X^T elements, and stores 4 X'^T elements, so every global
+// access of a wave covers whole 512-byte (bf16) rows.  A pass's X^T
+// elements are requested before its staging, at most 64 registers' worth
+// at a time (one memory round trip per pass for bf16 instead of one per few
+// chunks: with one block per CU nothing else hides that latency).
 template <typename T, int BT, int NW>
 __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                                 const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm,
@@ -419,12 +425,28 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
     using S = Shape<BT, NW>;
     constexpr int HB = BT / 2;   // X'^T rows per pass
     constexpr int NCH = BT / 4;  // 16-byte chunks (4 fp32) per staged row
+    constexpr int NPT = HB * NCH / S::kThreads;  // chunks per thread and pass
     static_assert(NCH >= 32, "swizzle range");
+    static_assert((HB * NCH) % S::kThreads == 0, "walk");
     float* st = reinterpret_cast<float*>(lds_raw);
     const int64_t ld = d.ld;  // row pitch of X^T and X'^T
+    using Raw = typename Vec4<T>::raw;
+    constexpr int PF = NPT * int(sizeof(Raw)) <= 256 ? NPT : 256 / int(sizeof(Raw));  // chunks per batch
+    static_assert(NPT % PF == 0, "batches");
+    Raw xv[PF];
+    auto gidx = [&](int h, int i) -> int64_t {
+        const int k = threadIdx.x + i * S::kThreads;
+        return int64_t(col0 + h * HB + k / NCH) * ld + row0 + (k % NCH) * 4;
+    };
+    auto load_batch = [&](int h, int b) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) xv[i] = Vec4<T>::load(XTin + gidx(h, b * PF + i));
+    };
+    load_batch(0, 0);
     __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        if (h == 1) load_batch(1, 0);
         if (wn / (S::WC / 2) == h) {
 #pragma unroll
             for (int mi = 0; mi < S::MM; ++mi)
@@ -441,15 +463,21 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
                     }
         }
         __syncthreads();
-#pragma unroll 4
-        for (int k = threadIdx.x; k < HB * NCH; k += S::kThreads) {
-            const int R = k / NCH, c = k % NCH;
-            const float4 v = *reinterpret_cast<const float4*>(st + R * BT + ((c ^ (R & 31)) * 4));
-            const int64_t gi = int64_t(col0 + h * HB + R) * ld + row0 + c * 4;
-            const typename Vec4<T>::raw xv = Vec4<T>::load(XTin + gi);
-            const float o[4] = {(a.ca * Vec4<T>::get(xv, 0) + v.x) * s1, (a.ca * Vec4<T>::get(xv, 1) + v.y) * s1,
-                                (a.ca * Vec4<T>::get(xv, 2) + v.z) * s1, (a.ca * Vec4<T>::get(xv, 3) + v.w) * s1};
-            Vec4<T>::store(XTout + gi, o);
+#pragma unroll
+        for (int b = 0; b < NPT / PF; ++b) {
+            if (b > 0) load_batch(h, b);
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                const int i = b * PF + j;
+                const int k = threadIdx.x + i * S::kThreads;
+                const int R = k / NCH, c = k % NCH;
+                const float4 v = *reinterpret_cast<const float4*>(st + R * BT + ((c ^ (R & 31)) * 4));
+                const float o[4] = {(a.ca * Vec4<T>::get(xv[j], 0) + v.x) * s1,
+                                    (a.ca * Vec4<T>::get(xv[j], 1) + v.y) * s1,
+                                    (a.ca * Vec4<T>::get(xv[j], 2) + v.z) * s1,
+                                    (a.ca * Vec4<T>::get(xv[j], 3) + v.w) * s1};
+                Vec4<T>::store(XTout + gidx(h, i), o);
+            }
         }
         __syncthreads();  // the staging area is free for the next pass
     }
@@ -510,6 +538,35 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// s_waitcnt vmcnt(VM) lgkmcnt(LGKM) through the builtin (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8), so the compiler's own
+// wait insertion knows which reads have returned; an inline-asm wait is
+// invisible to it and it then adds a full wait of its own at the next use.
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt_seen() {
+    static_assert(VM >= 0 && VM <= 63 && LGKM >= 0 && LGKM <= 15, "waitcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Direct-to-LDS load of 16 bytes per lane (buffer resource words rs in
+// scalar registers, LDS destination lds_addr in M0) issued through inline
+// assembly.  The compiler cannot tell its LDS reads from the LDS writes of
+// an outstanding direct-to-LDS load when the reads are the transposing
+// ones, and then waits for every outstanding load before each such read,
+// look-ahead loads included; loads it does not see are not ordered that way.
+// Completion is the caller's explicit vmcnt wait.  Nothing else in the
+// kernels that use it keeps a value in M0 (checked in the generated code);
+// the hazard after writing M0 takes one wait state.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_unseen(i32x4_t rs, uint32_t lds_addr, uint32_t voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_addr), "v"(voff),
+                 "s"(rs), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 #ifndef MFSDP_PINGPONG
 #define MFSDP_PINGPONG 1
 #endif
@@ -543,6 +600,24 @@ struct Ring32 {
     static constexpr bool value = MFSDP_RING32 && !PingPong<T, PHASE, BT, NW>::value && PipeFor<BT>::KSB == 128 &&
                                   PipeFor<BT>::NBUF == 2;
 };
+template <typename T, int PHASE, int BT, int NW>
+struct Lock4;
+
+// Locked schedule: one wave per SIMD (4 waves of 128 x 128 on 256 tiles,
+// bf16) issuing a fixed instruction order.  Each of the stage's four groups
+// of 16 MFMAs carries its side work between the MFMAs: the next sub-step's
+// fragment reads and the stage's direct-to-LDS loads.  Scheduling fences
+// keep the compiler from regrouping them (left to itself it moves every LDS
+// read next to its first use and then waits for it).  Same split 3/2 stage
+// rings as below.
+#ifndef MFSDP_LOCK4
+#define MFSDP_LOCK4 1
+#endif
+template <typename T, int PHASE, int BT, int NW>
+struct Lock4 {
+    static constexpr bool value = MFSDP_LOCK4 && sizeof(T) == 2 && BT == 256 && NW == 4 &&
+                                  PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
+};
 
 // LDS of the block: the main loop's operand stages (the split rings take 5
 // operand stages, the paired buffers 2 * NBUF); the epilogues reuse the same
@@ -550,7 +625,8 @@ struct Ring32 {
 template <typename T, int PHASE, int BT, int NW>
 struct LdsBytes {
     using PP = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>;
-    static constexpr int main_loop = Ring32<T, PHASE, BT, NW>::value ? 5 * PP::OPB : PP::BYTES;
+    static constexpr int main_loop =
+        (Ring32<T, PHASE, BT, NW>::value || Lock4<T, PHASE, BT, NW>::value) ? 5 * PP::OPB : PP::BYTES;
     static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
     static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
 };
@@ -709,6 +785,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             return out;
         }
     };
+    // one of the two transposing reads of a bf16 K-major fragment (h = 0:
+    // contraction indices k0..k0+3 of the lane's half, h = 1: k0+4..k0+7)
+    auto kmajor_half = [&](int off, int c, int kk, int h) -> u32x2_t {
+        const uint8_t* base = lds_raw + off;
+        const int g16 = lane >> 4, sl = lane & 15;
+        const int col = c + 16 * (g16 & 1) + 4 * (sl & 3);
+        const int k = kk * 16 + 8 * (g16 >> 1) + (sl >> 2) + 4 * h;
+        const int r0 = (col / CB) * KST + k;
+        const int gr = (col % CB) / GE, e = (col % GE) * 2;
+        return ds_read_tr16(base + r0 * 128 + swz_k(r0, gr) * 16 + e);
+    };
     auto rowmajor_frag = [&](int off, int r, int kk) -> u32x4_t {
         const uint8_t* base = lds_raw + off;
         return *reinterpret_cast<const u32x4_t*>(base + r * KSB + swz_r<GR>(r, 2 * kk + fhalf) * 16);
@@ -738,7 +825,113 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[i][jj], af[i], bf[jj]);
     };
 
-    if constexpr (Ring32<T, PHASE, BT, NW>::value) {
+    if constexpr (Lock4<T, PHASE, BT, NW>::value) {
+        // Stage t (P in ring slot t % 3, Q in slot 3 + t % 2) runs four groups
+        // of MM x MN MFMAs: the previous stage's sub-step 3 (its fragments
+        // were read before the barrier that ended it), then sub-steps 0, 1
+        // and 2.  Side work, spread evenly over each group's MFMAs: group 0
+        // loads Q of stage t + 1 into the Q slot stage t - 1 released, group
+        // 1 reads sub-step 1's fragments and loads P of stage t + 2 into the
+        // P slot stage t - 1 released, groups 2 and 3 read sub-steps 2 and 3
+        // (group 3 in its first half, so they have returned by its end).
+        // Then the wave waits for its loads of stage t + 1 (all but the LP
+        // most recent, P of t + 2), the barrier makes every wave's loads
+        // visible and frees stage t's slots, and the reads of stage t + 1's
+        // sub-step 0 are issued; the next stage's group 0 covers them.
+        static_assert(SUBS == 4, "locked schedule: four sub-steps per stage");
+        constexpr int NF = MM * MN;                    // MFMAs per group
+        constexpr int NR = (KM ? 2 : 1) * (MM + MN);   // LDS read instructions per sub-step
+        // read instruction r of sub-step kk's fragments, from slots oP, oQ
+        auto read_one = [&](int r, int oP, int oQ, int kk, u32x4_t (&fa)[MM], u32x4_t (&fb)[MN]) {
+            if constexpr (KM) {
+                const int f = r >> 1, h = r & 1;
+                const bool isA = f < MM;
+                const int c = isA ? wm * S::WTM + f * 32 : wn * S::WTN + (f - MM) * 32;
+                const u32x2_t v = kmajor_half(isA ? oP : oQ, c, kk, h);
+                if (isA) {
+                    fa[f][2 * h] = v[0];
+                    fa[f][2 * h + 1] = v[1];
+                } else {
+                    fb[f - MM][2 * h] = v[0];
+                    fb[f - MM][2 * h + 1] = v[1];
+                }
+            } else {
+                if (r < MM)
+                    fa[r] = rowmajor_frag(oP, wm * S::WTM + r * 32 + frow, kk);
+                else
+                    fb[r - MM] = rowmajor_frag(oQ, wn * S::WTN + (r - MM) * 32 + frow, kk);
+            }
+        };
+        // The Gram's loads go through dma16_unseen (its fragment reads are the
+        // transposing ones); the row-major phases use the builtin.
+        const uint64_t aP = reinterpret_cast<uint64_t>(P), aQ = reinterpret_cast<uint64_t>(Q);
+        const i32x4_t wP = {uni(int(uint32_t(aP))), uni(int(uint32_t(aP >> 32))), uni(bytesP), kRsrcWord3};
+        const i32x4_t wQ = {uni(int(uint32_t(aQ))), uni(int(uint32_t(aQ >> 32))), uni(bytesQ), kRsrcWord3};
+        const uint32_t lds0 =
+            uint32_t(uni(int(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds_raw))));
+        auto load_one = [&](bool isP, int kt, int off, int i) {
+            const int so = (isP ? uP[i] + kt * stepP : uQ[i] + kt * stepQ);
+            if constexpr (KM)
+                dma16_unseen(isP ? wP : wQ, lds0 + uint32_t(off + ldsd[i]), voff, so);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(isP ? rsP : rsQ,
+                                                         (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]),
+                                                         16, int(voff), so, 0, 0);
+        };
+        // One group: MFMA m of (fa, fb), then the side operations t with
+        // t * SPAN / n == m (side(t)), each pair fenced.
+        auto group = [&](const u32x4_t (&fa)[MM], const u32x4_t (&fb)[MN], int n, int span, auto&& side) {
+#pragma unroll
+            for (int m = 0; m < NF; ++m) {
+                Mfma<T>::step(acc[m / MN][m % MN], fa[m / MN], fb[m % MN]);
+#pragma unroll
+                for (int t = 0; t < n; ++t)
+                    if (t * span / n == m) side(t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < LP; ++i) load_one(true, 0, 0, i);
+#pragma unroll
+        for (int i = 0; i < LP; ++i) load_one(false, 0, 3 * OPB, i);
+#pragma unroll
+        for (int i = 0; i < LP; ++i) load_one(true, 1 < KT ? 1 : KT - 1, OPB, i);
+        waitcnt_seen<LP, 0>();
+        __builtin_amdgcn_s_barrier();
+        u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
+#pragma unroll
+        for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(r, 0, 3 * OPB, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        int sp = 0, sq = 0;  // P and Q slots of stage kt
+        for (int kt = 0; kt < KT; ++kt) {
+            const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
+            const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
+            const int oP = sp * OPB, oQ = (3 + sq) * OPB;
+            const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
+            group(fa1, fb1, LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
+            group(fa0, fb0, NR + LP, NF, [&](int t) {
+                if (t < NR)
+                    read_one(t, oP, oQ, 1, fa1, fb1);
+                else
+                    load_one(true, kp, oPn, t - NR);
+            });
+            group(fa1, fb1, NR, NF, [&](int t) { read_one(t, oP, oQ, 2, fa0, fb0); });
+            group(fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
+            waitcnt_seen<LP, 0>();
+            __builtin_amdgcn_s_barrier();
+            sp = sp == 2 ? 0 : sp + 1;
+            sq ^= 1;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, (3 + sq) * OPB, 0, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfmas(fa1, fb1);  // last sub-step of the last stage
+        wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
+    } else if constexpr (Ring32<T, PHASE, BT, NW>::value) {
         // Split rings: P's stage slots form a ring of 3 (byte offsets 0, OPB,
         // 2*OPB), Q's a ring of 2 (3*OPB, 4*OPB).  During stage t the block
         // loads Q of stage t + 1 and then P of stage t + 2, each into the slot
@@ -968,7 +1161,7 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
 // Wave count of the 256-tile kernels (4: one wave per SIMD with 128x128 each;
 // 8: two per SIMD with 128x64 each, measured faster).
 #ifndef MFSDP_WAVES_256
-#define MFSDP_WAVES_256 8
+#define MFSDP_WAVES_256 4
 #endif
 
 template <typename T, int PHASE>
@@ -977,7 +1170,7 @@ void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
     if (n_tiles <= 0) return;
     const int grid = n_tiles;
     if (tile == 256) {
-        constexpr int NW = MFSDP_WAVES_256;
+        constexpr int NW = PHASE == kFinal ? 8 : MFSDP_WAVES_256;
         k_ns_gemm<T, PHASE, 256, NW><<<dim3(grid), dim3(64 * NW), 0, stream>>>(a);
     } else {
         k_ns_gemm<T, PHASE, 128, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
