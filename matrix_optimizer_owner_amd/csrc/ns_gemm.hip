@@ -279,57 +279,71 @@ __device__ __forceinline__ void w_update4(WT_* w, float* o_out, const float* o, 
 // In two halves of the tile's rows: every lane reads X from X^T (its 4
 // accumulator rows are 4 consecutive elements there), writes O into an LDS
 // tile laid out in W's orientation, then the block walks that tile in W's
-// memory order with 4-element vectors (coalesced W loads and stores).
-template <typename T, int BT, int NW>
-__device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
-                                             const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
-                                             int frow, int fhalf, float s1, const T* XTin, float* olds) {
+// memory order with 4-element vectors (coalesced W loads and stores).  On
+// tiles inside W with 4-aligned rows, a half's W chunks (at most 64
+// registers' worth at a time, 32 with fp32 Newton-Schulz) are requested before its O tile is built, so
+// a half costs about one memory round trip; edge tiles take a scalar walk.
+// Element offsets into W fit in 32 bits: the planner keeps every padded
+// matrix below 2^30 elements.
+template <typename T, int BT, int NW, bool TR, typename WT_>
+__device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                               const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
+                                               int frow, int fhalf, float s1, const T* XTin, float* olds, WT_* W) {
     using S = Shape<BT, NW>;
     using L = FinalLds<BT>;
+    using Raw = typename Vec4<WT_>::raw;
     constexpr int HW = S::WTM / 2;  // rows of one wave's block per half
-    const bool tr = d.transposed != 0;
+    constexpr int CHUNKS = L::HR * BT / 4;
+    constexpr int NPT = CHUNKS / S::kThreads;  // chunks of 4 elements per thread and half
+    constexpr int PFB = sizeof(T) == 2 ? 256 : 128;  // prefetch bytes per lane (fp32 X^T needs more registers)
+    constexpr int PF = NPT * int(sizeof(Raw)) <= PFB ? NPT : PFB / int(sizeof(Raw));  // chunks per batch
+    static_assert(CHUNKS % S::kThreads == 0 && NPT % PF == 0, "walk");
     const float step = a.lr * d.lr_scale;
-    const int64_t ld = d.ld;  // row pitch of X^T
-    const int64_t ldw = d.cols;
-    const bool vec = (d.cols & 3) == 0;
-    uint8_t* Wb = a.params + d.param_off;
+    const uint32_t ld = uint32_t(d.ld);  // row pitch of X^T
+    const int ldw = d.cols;
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;
     const int w_rows = d.rows, w_cols = d.cols;
     const int j = frow & 3;
-    // The O tile reuses the operand stages: every wave's last direct-to-LDS
-    // loads (the main loop's look-ahead past the end) must have landed.
-    __syncthreads();
+    // W rows / columns the tile covers: tile rows are W columns when W is
+    // stored transposed to X
+    const bool inside = (d.cols & 3) == 0 && (TR ? (col0 + BT <= w_rows && row0 + BT <= w_cols)
+                                                 : (row0 + BT <= w_rows && col0 + BT <= w_cols));
 
+    // chunk c of the thread in half h: LDS offset, W element offset, valid count
+    auto chunk = [&](int h, int c, int& lofs, int& widx, int& n_ok) {
+        const int k = threadIdx.x + c * S::kThreads;
+        if constexpr (TR) {
+            const int lc = k / (L::HR / 4);
+            const int lr = (k % (L::HR / 4)) * 4;
+            lofs = lc * L::PT + lr;
+            const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;  // tile row -> W column
+            const int gc = col0 + lc;                                     // tile column -> W row
+            widx = gc * ldw + gr;
+            n_ok = gc < w_rows ? min(4, w_cols - gr) : 0;
+        } else {
+            const int lr = k / (BT / 4);
+            const int lc = (k % (BT / 4)) * 4;
+            lofs = lr * L::PN + lc;
+            const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;
+            const int gc = col0 + lc;
+            widx = gr * ldw + gc;
+            n_ok = gr < w_rows ? min(4, w_cols - gc) : 0;
+        }
+    };
+    Raw raw[PF];
+    auto load_batch = [&](int h, int b) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            int lofs, widx, n_ok;
+            chunk(h, b * PF + i, lofs, widx, n_ok);
+            raw[i] = Vec4<WT_>::load(W + widx);
+        }
+    };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        // The block walks the half tile in W's memory order, 4 elements per
-        // chunk; a thread owns chunks threadIdx.x + j * kThreads and issues the
-        // W loads of a batch of chunks (8 for bf16, 4 for fp32) before it
-        // consumes any: one W round trip per batch.
-        constexpr int CHUNKS = L::HR * BT / 4;
-        constexpr int NPT = CHUNKS / S::kThreads;
-        static_assert(CHUNKS % S::kThreads == 0, "walk");
-        auto chunk = [&](int j, int& lofs, int64_t& widx, int& n_ok) {
-            const int k = threadIdx.x + j * S::kThreads;
-            if (tr) {
-                const int lc = k / (L::HR / 4);
-                const int lr = (k % (L::HR / 4)) * 4;
-                lofs = lc * L::PT + lr;
-                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;  // tile row -> W column
-                const int gc = col0 + lc;                                     // tile column -> W row
-                widx = int64_t(gc) * ldw + gr;
-                n_ok = gc < w_rows ? min(4, w_cols - gr) : 0;
-            } else {
-                const int lr = k / (BT / 4);
-                const int lc = (k % (BT / 4)) * 4;
-                lofs = lr * L::PN + lc;
-                const int gr = row0 + (lr / HW) * S::WTM + h * HW + lr % HW;
-                const int gc = col0 + lc;
-                widx = int64_t(gr) * ldw + gc;
-                n_ok = gr < w_rows ? min(4, w_cols - gc) : 0;
-            }
-        };
-        // 1) O for this half into LDS, in W's orientation
+        if (inside) load_batch(h, 0);
+        // 1) O for this half into LDS, in W's orientation (X^T elements of
+        // one MFMA row block at a time)
 #pragma unroll
         for (int mh = 0; mh < S::MM / 2; ++mh) {
             const int mi = h * (S::MM / 2) + mh;
@@ -340,7 +354,7 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
                 for (int q = 0; q < 4; ++q) {
                     const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
                     const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                    xv[ni][q] = Vec4<T>::load(XTin + int64_t(c) * ld + rb);
+                    xv[ni][q] = Vec4<T>::load(XTin + (uint32_t(c) * ld + uint32_t(rb)));
                 }
 #pragma unroll
             for (int ni = 0; ni < S::MN; ++ni)
@@ -352,7 +366,7 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         o[e] = (a.ca * Vec4<T>::get(xv[ni][q], e) + acc[mi][ni][q * 4 + e]) * s1;
-                    if (tr) {
+                    if constexpr (TR) {
                         *reinterpret_cast<float4*>(olds + lc * L::PT + lr) = make_float4(o[0], o[1], o[2], o[3]);
                     } else {
                         quad_transpose(o, j);  // row lr + j, columns lc - j .. lc - j + 3
@@ -362,48 +376,65 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
                 }
         }
         __syncthreads();
-        // 2) walk the half tile in W's memory order (see above)
-        auto walk = [&](auto* W) {
-            using WT_ = typename std::remove_pointer<decltype(W)>::type;
-            constexpr int NB0 = sizeof(WT_) == 2 ? 8 : 4;  // W loads in flight
-            constexpr int NB = NPT < NB0 ? NPT : NB0;
-            static_assert(NPT % NB == 0, "batches");
+        // 2) walk the half tile in W's memory order
+        if (inside) {
 #pragma unroll
-            for (int j0 = 0; j0 < NPT; j0 += NB) {
-                typename Vec4<WT_>::raw raw[NB];
-                int64_t widx[NB];
-                int n_ok[NB], lofs[NB];
+            for (int b = 0; b < NPT / PF; ++b) {
+                if (b > 0) load_batch(h, b);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    chunk(j0 + b, lofs[b], widx[b], n_ok[b]);
-                    if (vec && n_ok[b] == 4) raw[b] = Vec4<WT_>::load(W + widx[b]);
-                }
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (n_ok[b] <= 0) continue;
-                    const float4 v = *reinterpret_cast<const float4*>(olds + lofs[b]);
+                for (int i = 0; i < PF; ++i) {
+                    int lofs, widx, n_ok;
+                    chunk(h, b * PF + i, lofs, widx, n_ok);
+                    const float4 v = *reinterpret_cast<const float4*>(olds + lofs);
                     const float o[4] = {v.x, v.y, v.z, v.w};
-                    float* op = O ? O + widx[b] : nullptr;
-                    if (vec && n_ok[b] == 4) {
-                        float r[4];
+                    float r[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float x = Vec4<WT_>::get(raw[b], e);
-                            r[e] = __builtin_fmaf(-step, o[e], __builtin_fmaf(-a.lrwd, x, x));
-                        }
-                        Vec4<WT_>::store(W + widx[b], r);
-                        if (op) *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
-                    } else {
-                        w_update4<WT_>(W + widx[b], op, o, a.lrwd, step, n_ok[b], false);
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = Vec4<WT_>::get(raw[i], e);
+                        r[e] = __builtin_fmaf(-step, o[e], __builtin_fmaf(-a.lrwd, x, x));
                     }
+                    Vec4<WT_>::store(W + widx, r);
+                    if (O) *reinterpret_cast<float4*>(O + widx) = v;
                 }
             }
-        };
-        if (d.dtype == kBF16)
-            walk(reinterpret_cast<uint16_t*>(Wb));
-        else
-            walk(reinterpret_cast<float*>(Wb));
+        } else {
+#pragma unroll 1
+            for (int c = 0; c < NPT; ++c) {
+                int lofs, widx, n_ok;
+                chunk(h, c, lofs, widx, n_ok);
+                if (n_ok <= 0) continue;
+                const float4 v = *reinterpret_cast<const float4*>(olds + lofs);
+                const float o[4] = {v.x, v.y, v.z, v.w};
+                w_update4<WT_>(W + widx, O ? O + widx : nullptr, o, a.lrwd, step, n_ok,
+                               (d.cols & 3) == 0 && n_ok == 4);
+            }
+        }
         __syncthreads();
+    }
+}
+
+template <typename T, int BT, int NW>
+__device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                             const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
+                                             int frow, int fhalf, float s1, const T* XTin, float* olds) {
+    // The O tile reuses the operand stages: every wave's last direct-to-LDS
+    // loads (the main loop's look-ahead past the end) must have landed.
+    __syncthreads();
+    uint8_t* Wb = a.params + d.param_off;
+    if (d.transposed) {
+        if (d.dtype == kBF16)
+            final_update_t<T, BT, NW, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+                                            reinterpret_cast<uint16_t*>(Wb));
+        else
+            final_update_t<T, BT, NW, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+                                            reinterpret_cast<float*>(Wb));
+    } else {
+        if (d.dtype == kBF16)
+            final_update_t<T, BT, NW, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+                                             reinterpret_cast<uint16_t*>(Wb));
+        else
+            final_update_t<T, BT, NW, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+                                             reinterpret_cast<float*>(Wb));
     }
 }
 
@@ -1170,7 +1201,7 @@ void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
     if (n_tiles <= 0) return;
     const int grid = n_tiles;
     if (tile == 256) {
-        constexpr int NW = PHASE == kFinal ? 8 : MFSDP_WAVES_256;
+        constexpr int NW = MFSDP_WAVES_256;
         k_ns_gemm<T, PHASE, 256, NW><<<dim3(grid), dim3(64 * NW), 0, stream>>>(a);
     } else {
         k_ns_gemm<T, PHASE, 128, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
