@@ -71,6 +71,11 @@ template <> struct Mfma<uint16_t> {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
     }
+    // a * b with a zero accumulator input
+    __device__ __forceinline__ static f32x16_t first(const u32x4_t& a, const u32x4_t& b) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), f32x16_t{}, 0, 0, 0);
+    }
 };
 template <> struct Mfma<float> {
     __device__ __forceinline__ static void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
@@ -284,8 +289,9 @@ __device__ __forceinline__ void w_update4(WT_* w, float* o_out, const float* o, 
 // registers' worth at a time, 32 with fp32 Newton-Schulz) are requested before its O tile is built, so
 // a half costs about one memory round trip; edge tiles take a scalar walk.
 // Element offsets into W fit in 32 bits: the planner keeps every padded
-// matrix below 2^30 elements.
-template <typename T, int BT, int NW, bool TR, typename WT_>
+// matrix below 2^30 elements.  When AX is false the main loop has already
+// added a X to the accumulators.
+template <typename T, int BT, int NW, bool AX, bool TR, typename WT_>
 __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                                const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
                                                int frow, int fhalf, float s1, const T* XTin, float* olds, WT_* W) {
@@ -348,14 +354,16 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
         for (int mh = 0; mh < S::MM / 2; ++mh) {
             const int mi = h * (S::MM / 2) + mh;
             typename Vec4<T>::raw xv[S::MN][4];
+            if constexpr (AX) {
 #pragma unroll
-            for (int ni = 0; ni < S::MN; ++ni)
+                for (int ni = 0; ni < S::MN; ++ni)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
-                    const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                    xv[ni][q] = Vec4<T>::load(XTin + (uint32_t(c) * ld + uint32_t(rb)));
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
+                        const int c = col0 + wn * S::WTN + ni * 32 + frow;
+                        xv[ni][q] = Vec4<T>::load(XTin + (uint32_t(c) * ld + uint32_t(rb)));
+                    }
+            }
 #pragma unroll
             for (int ni = 0; ni < S::MN; ++ni)
 #pragma unroll
@@ -365,7 +373,8 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
                     float o[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        o[e] = (a.ca * Vec4<T>::get(xv[ni][q], e) + acc[mi][ni][q * 4 + e]) * s1;
+                        o[e] = AX ? (a.ca * Vec4<T>::get(xv[ni][q], e) + acc[mi][ni][q * 4 + e]) * s1
+                                  : acc[mi][ni][q * 4 + e] * s1;
                     if constexpr (TR) {
                         *reinterpret_cast<float4*>(olds + lc * L::PT + lr) = make_float4(o[0], o[1], o[2], o[3]);
                     } else {
@@ -413,7 +422,7 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
     }
 }
 
-template <typename T, int BT, int NW>
+template <typename T, int BT, int NW, bool AX>
 __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                              const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm, int wn,
                                              int frow, int fhalf, float s1, const T* XTin, float* olds) {
@@ -423,17 +432,17 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
     uint8_t* Wb = a.params + d.param_off;
     if (d.transposed) {
         if (d.dtype == kBF16)
-            final_update_t<T, BT, NW, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+            final_update_t<T, BT, NW, AX, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
                                             reinterpret_cast<uint16_t*>(Wb));
         else
-            final_update_t<T, BT, NW, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+            final_update_t<T, BT, NW, AX, true>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
                                             reinterpret_cast<float*>(Wb));
     } else {
         if (d.dtype == kBF16)
-            final_update_t<T, BT, NW, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+            final_update_t<T, BT, NW, AX, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
                                              reinterpret_cast<uint16_t*>(Wb));
         else
-            final_update_t<T, BT, NW, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
+            final_update_t<T, BT, NW, AX, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, olds,
                                              reinterpret_cast<float*>(Wb));
     }
 }
@@ -447,8 +456,9 @@ __device__ __forceinline__ void final_update(const f32x16_t (&acc)[Shape<BT, NW>
 // access of a wave covers whole 512-byte (bf16) rows.  A pass's X^T
 // elements are requested before its staging, at most 64 registers' worth
 // at a time (one memory round trip per pass for bf16 instead of one per few
-// chunks: with one block per CU nothing else hides that latency).
-template <typename T, int BT, int NW>
+// chunks: with one block per CU nothing else hides that latency).  When AX
+// is false the main loop has already added a X to the accumulators.
+template <typename T, int BT, int NW, bool AX>
 __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                                 const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm,
                                                 int wn, int frow, int fhalf, float s1, const T* XTin, T* XTout,
@@ -473,11 +483,11 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
 #pragma unroll
         for (int i = 0; i < PF; ++i) xv[i] = Vec4<T>::load(XTin + gidx(h, b * PF + i));
     };
-    load_batch(0, 0);
+    if constexpr (AX) load_batch(0, 0);
     __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (h == 1) load_batch(1, 0);
+        if (AX && h == 1) load_batch(1, 0);
         if (wn / (S::WC / 2) == h) {
 #pragma unroll
             for (int mi = 0; mi < S::MM; ++mi)
@@ -496,17 +506,18 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < NPT / PF; ++b) {
-            if (b > 0) load_batch(h, b);
+            if (AX && b > 0) load_batch(h, b);
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
                 const int i = b * PF + j;
                 const int k = threadIdx.x + i * S::kThreads;
                 const int R = k / NCH, c = k % NCH;
                 const float4 v = *reinterpret_cast<const float4*>(st + R * BT + ((c ^ (R & 31)) * 4));
-                const float o[4] = {(a.ca * Vec4<T>::get(xv[j], 0) + v.x) * s1,
-                                    (a.ca * Vec4<T>::get(xv[j], 1) + v.y) * s1,
-                                    (a.ca * Vec4<T>::get(xv[j], 2) + v.z) * s1,
-                                    (a.ca * Vec4<T>::get(xv[j], 3) + v.w) * s1};
+                float o[4] = {v.x * s1, v.y * s1, v.z * s1, v.w * s1};
+                if constexpr (AX) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = (a.ca * Vec4<T>::get(xv[j], e) + (&v.x)[e]) * s1;
+                }
                 Vec4<T>::store(XTout + gidx(h, i), o);
             }
         }
@@ -671,6 +682,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     constexpr int SUBS = PP::SUBS, GR = PP::GR, OPB = PP::OPB;
     // the Gram's operands are K-major (X^T rows are the contraction index)
     constexpr bool KM = PHASE == kGram;
+    // the update phases of the locked loop add a X inside the main loop
+    constexpr bool kFoldAX = Lock4<T, PHASE, BT, NW>::value && (PHASE == kUpdate || PHASE == kFinal);
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
@@ -909,18 +922,56 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                                                          (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]),
                                                          16, int(voff), so, 0, 0);
         };
-        // One group: MFMA m of (fa, fb), then the side operations t with
-        // t * SPAN / n == m (side(t)), each pair fenced.
-        auto group = [&](const u32x4_t (&fa)[MM], const u32x4_t (&fb)[MN], int n, int span, auto&& side) {
+        // One group: MFMA m of (fa, fb) (FIRST: with a zero accumulator input,
+        // starting the tile's accumulators; NONE: no MFMAs), then the side
+        // operations t with t * span / n == m (side(t)), each pair fenced.
+        auto group_k = [&](auto FIRST, auto NONE, const u32x4_t (&fa)[MM], const u32x4_t (&fb)[MN], int n, int span,
+                           auto&& side) {
 #pragma unroll
             for (int m = 0; m < NF; ++m) {
-                Mfma<T>::step(acc[m / MN][m % MN], fa[m / MN], fb[m % MN]);
+                if constexpr (decltype(FIRST)::value)
+                    acc[m / MN][m % MN] = Mfma<T>::first(fa[m / MN], fb[m % MN]);
+                else if constexpr (!decltype(NONE)::value)
+                    Mfma<T>::step(acc[m / MN][m % MN], fa[m / MN], fb[m % MN]);
 #pragma unroll
                 for (int t = 0; t < n; ++t)
                     if (t * span / n == m) side(t);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        using F0 = std::false_type;
+        using F1 = std::true_type;
+        // a X folded into the accumulators (update phases): X^T[n][k] sits in
+        // Q's stage slot, so in the sub-steps whose contraction indices k0 ..
+        // k0+15 fall in this wave's output rows m, the MFMA of an identity
+        // fragment with Q's fragments adds a * X[m][n] for those rows, a split
+        // as ahi + alo in bf16 (two MFMAs, products exact in fp32).  Lane
+        // (frow, fhalf) of an identity fragment holds contraction indices
+        // 8*fhalf .. 8*fhalf+7 of row frow: one nonzero when the sub-step
+        // starts ro = 16*RO rows into the 32-row MFMA block BLK.  The
+        // fragments are rebuilt at each use (a few VALU operations) rather
+        // than held in 16 registers across the loop.
+        const uint16_t ahi = f32_to_bf16(a.ca);
+        const uint16_t alo = f32_to_bf16(a.ca - bf16_to_f32(ahi));
+        auto fold = [&](auto blk, auto ro, const u32x4_t (&fb)[MN]) {
+            int t = frow - 16 * decltype(ro)::value - 8 * fhalf;
+            asm volatile("" : "+v"(t));  // keeps the fragments out of loop-invariant hoisting
+            u32x4_t ih, il;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const bool on = t >= 0 && t < 8 && (t >> 1) == w;
+                ih[w] = on ? uint32_t(ahi) << (16 * (t & 1)) : 0u;
+                il[w] = on ? uint32_t(alo) << (16 * (t & 1)) : 0u;
+            }
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], ih, fb[jj]);
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], il, fb[jj]);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I3 = std::integral_constant<int, 3>;
 #pragma unroll
         for (int i = 0; i < LP; ++i) load_one(true, 0, 0, i);
 #pragma unroll
@@ -931,27 +982,50 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         __builtin_amdgcn_s_barrier();
         u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
 #pragma unroll
-        for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
         for (int r = 0; r < NR; ++r) read_one(r, 0, 3 * OPB, 0, fa0, fb0);
         __builtin_amdgcn_sched_barrier(0);
         int sp = 0, sq = 0;  // P and Q slots of stage kt
-        for (int kt = 0; kt < KT; ++kt) {
+        // One stage; H = 0 / 1: first / second stage of a pair.  The wave's
+        // rows rows_u .. rows_u+127 (rows_u a multiple of 128) are the
+        // contraction indices of the stage pair p0 = rows_u / (2*KST): the
+        // identity MFMAs of its 8 sub-steps sit at fixed places of the pair
+        // (sub-step u of stage 2*p0 + H covers rows 64*H + 16*u: MFMA block
+        // 2*H + u/2, offset 16*(u%2)), under the uniform flags fold_a
+        // (sub-step 3 of the previous stage, run first here) and fold_r (this
+        // stage's sub-steps 0-2).  FIRST: the tile's stage 0, with no
+        // deferred sub-step before it.
+        auto stage = [&](int kt, auto H, bool fold_a, bool fold_r, auto FIRST) {
+            constexpr int hh = decltype(H)::value;
+            constexpr bool first = decltype(FIRST)::value;
             const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
             const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
             const int oP = sp * OPB, oQ = (3 + sq) * OPB;
             const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
-            group(fa1, fb1, LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
-            group(fa0, fb0, NR + LP, NF, [&](int t) {
+            if constexpr (kFoldAX && !first) {
+                if (fold_a) {
+                    if constexpr (hh == 0)
+                        fold(I3{}, I1{}, fb1);  // sub-step 3 of the second stage of the previous pair
+                    else
+                        fold(I1{}, I1{}, fb1);  // sub-step 3 of the first stage of this pair
+                }
+            }
+            group_k(F0{}, FIRST, fa1, fb1, LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
+            if constexpr (kFoldAX && !first)
+                if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
+            group_k(FIRST, F0{}, fa0, fb0, NR + LP, NF, [&](int t) {
                 if (t < NR)
                     read_one(t, oP, oQ, 1, fa1, fb1);
                 else
                     load_one(true, kp, oPn, t - NR);
             });
-            group(fa1, fb1, NR, NF, [&](int t) { read_one(t, oP, oQ, 2, fa0, fb0); });
-            group(fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
+            if constexpr (kFoldAX && first)
+                if (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
+            if constexpr (kFoldAX)
+                if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
+            group_k(F0{}, F0{}, fa1, fb1, NR, NF, [&](int t) { read_one(t, oP, oQ, 2, fa0, fb0); });
+            if constexpr (kFoldAX)
+                if (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
+            group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
             waitcnt_seen<LP, 0>();
             __builtin_amdgcn_s_barrier();
             sp = sp == 2 ? 0 : sp + 1;
@@ -959,7 +1033,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
             for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, (3 + sq) * OPB, 0, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
+        };
+        // (KT = K / KST is a multiple of 4: K is a multiple of 256)
+        const int p0 = (row0 + (wave_u / S::WC) * S::WTM) / (2 * KST);  // uniform (wave_u)
+        stage(0, I0{}, false, kFoldAX && p0 == 0, F1{});
+        stage(1, I1{}, kFoldAX && p0 == 0, kFoldAX && p0 == 0, F0{});
+        for (int p = 1; p < KT / 2; ++p) {
+            stage(2 * p, I0{}, kFoldAX && p - 1 == p0, kFoldAX && p == p0, F0{});
+            stage(2 * p + 1, I1{}, kFoldAX && p == p0, kFoldAX && p == p0, F0{});
         }
+        if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
         mfmas(fa1, fb1);  // last sub-step of the last stage
         wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
     } else if constexpr (Ring32<T, PHASE, BT, NW>::value) {
@@ -1121,11 +1204,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     const float s1 = a.first ? a.s[tile.mat] : 1.f;
     const int j = frow & 3;
     if constexpr (PHASE == kFinal) {
-        final_update<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
+        final_update<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
                                 reinterpret_cast<float*>(lds_raw));
         return;
     } else if constexpr (PHASE == kUpdate) {
-        update_epilogue<T, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
+        update_epilogue<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
                                    reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0])), lds_raw);
         return;
     } else {
