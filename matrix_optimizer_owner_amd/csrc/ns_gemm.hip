@@ -20,17 +20,20 @@
 //
 // Every launch covers every matrix of the owner buffer: the block index
 // selects a tile from a host-built list sorted longest-contraction first.
-// 256x256 output tiles with 8 wave64s (two per SIMD, each 128x64 as 4x2
+// 256x256 output tiles with 4 wave64s (one per SIMD, each 128x128 as 4x4
 // MFMA 32x32 tiles), or 128x128 tiles with 4 waves (two blocks per CU) for
 // phases with too few large tiles to fill the chip.  Operands reach LDS by
 // direct global->LDS loads in 128-byte rows (64 bf16 or 32 fp32 of the
-// contraction index per stage): the bf16 Gram on 256 tiles in two paired
-// stage buffers with a ping-pong schedule, every other phase in split stage
-// rings (3 for P, 2 for Q).  Operands that are contiguous along the
-// contraction are read back with 16-byte fragment reads; the Gram's K-major
-// X^T is read back with the transposing LDS read (ds_read_b64_tr_b16), so X
-// is kept only as X^T.  bf16 uses v_mfma_f32_32x32x16_bf16; fp32 uses
-// v_mfma_f32_32x32x2_f32 (four per 8-element granule pair).
+// contraction index per stage) into split stage rings (3 slots for P, 2 for
+// Q).  bf16 on 256 tiles runs a locked instruction schedule (MFMAs, fragment
+// reads and loads interleaved in a fixed order, over stage pairs) and, in
+// the update phases, adds a X through identity-fragment MFMAs; the other
+// kernels run a compiler-scheduled loop.  Operands that are contiguous along
+// the contraction are read back with 16-byte fragment reads; the Gram's
+// K-major X^T is read back with the transposing LDS read
+// (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
+// v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
+// 8-element granule pair).
 #include <type_traits>
 
 #include "device_util.h"
@@ -194,40 +197,21 @@ struct Shape {
     static constexpr int MN = WTN / 32;          // MFMA tiles per wave along columns
 };
 
-// Main-loop pipeline: stages of KSB bytes of contraction index (two MFMA
-// sub-steps of 32 bytes per 64), NBUF stage buffers in LDS, loads issued
-// NBUF - 1 stages ahead.
-template <int BT, int NW, int KSB, int NBUF>
+// Main-loop pipeline: stages of KSB = 128 bytes of contraction index (four
+// MFMA sub-steps of 32 bytes) in split stage rings of 3 P slots and 2 Q
+// slots (5 operand stages of LDS: 160 KB for 256 tiles, 80 KB for 128
+// tiles).  On the Llama-3-8B share, 64-byte stages with more look-ahead
+// (twice the barriers) measured 10-20% slower.
+template <int BT, int NW>
 struct Pipe {
+    static constexpr int KSB = 128;                // bytes of contraction index per stage
     static constexpr int SUBS = KSB / 32;          // MFMA sub-steps per stage
     static constexpr int GR = KSB / 16;            // 16-byte granules per row-major LDS row
     static constexpr int OPB = BT * KSB;           // bytes of one operand's stage
     static constexpr int LP = OPB / (1024 * NW);   // direct-to-LDS loads per wave, operand and stage
-    static constexpr int BYTES = NBUF * 2 * OPB;
-    static_assert(SUBS % 2 == 0 && LP >= 1 && OPB % (1024 * NW) == 0, "pipeline shape");
-    static_assert(NBUF >= 2 && 2 * LP * (NBUF - 2) <= 63, "vmcnt range");
+    static constexpr int BYTES = 5 * OPB;          // the two rings
+    static_assert(SUBS % 2 == 0 && LP >= 1 && OPB % (1024 * NW) == 0 && 2 * LP <= 63, "pipeline shape");
 };
-
-// Stage geometry per tile edge: (KSB, NBUF) of the paired layout, where a
-// stage buffer holds both operands (the ping-pong Gram; the split rings use
-// the same 128-byte stages in 5 operand slots).  On the Llama-3-8B share,
-// 64-byte stages with 3 to 5 paired buffers (more look-ahead, twice the
-// barriers) measured 10-20% slower than 128-byte stages.
-#ifndef MFSDP_KSB_256
-#define MFSDP_KSB_256 128
-#endif
-#ifndef MFSDP_NBUF_256
-#define MFSDP_NBUF_256 2
-#endif
-#ifndef MFSDP_KSB_128
-#define MFSDP_KSB_128 128
-#endif
-#ifndef MFSDP_NBUF_128
-#define MFSDP_NBUF_128 2
-#endif
-template <int BT> struct PipeFor;
-template <> struct PipeFor<256> { static constexpr int KSB = MFSDP_KSB_256, NBUF = MFSDP_NBUF_256; };
-template <> struct PipeFor<128> { static constexpr int KSB = MFSDP_KSB_128, NBUF = MFSDP_NBUF_128; };
 
 // LDS tile of the final update (one half of the tile's rows at a time), in
 // W's orientation: [BT/2][BT+4] floats when W is not transposed, else
@@ -562,14 +546,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Block barrier between ping-pong phases: the wave's LDS reads have returned
-// (the buffer they read may be refilled next phase), nothing is moved across.
-__device__ __forceinline__ void phase_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // Block barrier between main-loop stages.  __syncthreads() is a workgroup
 // release fence and waits for every outstanding vector-memory load
 // (vmcnt(0)), which would also wait for look-ahead loads of later stages;
@@ -609,66 +585,23 @@ __device__ __forceinline__ void dma16_unseen(i32x4_t rs, uint32_t lds_addr, uint
 }
 #pragma clang diagnostic pop
 
-#ifndef MFSDP_PINGPONG
-#define MFSDP_PINGPONG 1
-#endif
-#ifndef MFSDP_PP_BURST
-#define MFSDP_PP_BURST 4  // MFMA sub-steps per ping-pong phase
-#endif
-#ifndef MFSDP_RING32
-#define MFSDP_RING32 1
-#endif
-
-// The ping-pong schedule serves the bf16 Gram on 256 tiles with 8 waves and
-// 128-byte stages in two paired buffers.  On the Llama-3-8B share it made
-// the Gram 2-7% faster (its transposing fragment reads are twice as many
-// instructions, which batch better than they interleave) and the row-major
-// phases slower; half-stage bursts were slower for all three.
-template <typename T, int PHASE, int BT, int NW>
-struct PingPong {
-    static constexpr bool value = MFSDP_PINGPONG && sizeof(T) == 2 && PHASE == kGram && BT == 256 && NW == 8 &&
-                                  PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
-};
-
-// Split 3/2 stage rings (P loaded two stages ahead) serve every phase that
-// does not run the ping-pong, with 128-byte stages; they take 5 operand
-// stages of LDS (160 KB for 256 tiles, 80 KB for 128 tiles).  On the
-// Llama-3-8B share they measured about 1% faster than two paired buffers;
-// look-ahead beyond that (64-byte stages in 3 to 5 buffers, or an L2
-// prefetch of later stages) was slower: the stage time is set by the volume
-// of loads per CU rather than by their latency.
-template <typename T, int PHASE, int BT, int NW>
-struct Ring32 {
-    static constexpr bool value = MFSDP_RING32 && !PingPong<T, PHASE, BT, NW>::value && PipeFor<BT>::KSB == 128 &&
-                                  PipeFor<BT>::NBUF == 2;
-};
-template <typename T, int PHASE, int BT, int NW>
-struct Lock4;
-
 // Locked schedule: one wave per SIMD (4 waves of 128 x 128 on 256 tiles,
 // bf16) issuing a fixed instruction order.  Each of the stage's four groups
 // of 16 MFMAs carries its side work between the MFMAs: the next sub-step's
 // fragment reads and the stage's direct-to-LDS loads.  Scheduling fences
 // keep the compiler from regrouping them (left to itself it moves every LDS
-// read next to its first use and then waits for it).  Same split 3/2 stage
-// rings as below.
-#ifndef MFSDP_LOCK4
-#define MFSDP_LOCK4 1
-#endif
+// read next to its first use and then waits for it).  The other kernels
+// (fp32, 128 tiles) run the compiler-scheduled loop over the same rings.
 template <typename T, int PHASE, int BT, int NW>
 struct Lock4 {
-    static constexpr bool value = MFSDP_LOCK4 && sizeof(T) == 2 && BT == 256 && NW == 4 &&
-                                  PipeFor<BT>::KSB == 128 && PipeFor<BT>::NBUF == 2;
+    static constexpr bool value = sizeof(T) == 2 && BT == 256 && NW == 4;
 };
 
-// LDS of the block: the main loop's operand stages (the split rings take 5
-// operand stages, the paired buffers 2 * NBUF); the epilogues reuse the same
-// bytes (the final update slightly more of them for its O tile).
+// LDS of the block: the main loop's 5 operand stages; the epilogues reuse
+// the same bytes (the final update slightly more of them for its O tile).
 template <typename T, int PHASE, int BT, int NW>
 struct LdsBytes {
-    using PP = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>;
-    static constexpr int main_loop =
-        (Ring32<T, PHASE, BT, NW>::value || Lock4<T, PHASE, BT, NW>::value) ? 5 * PP::OPB : PP::BYTES;
+    static constexpr int main_loop = Pipe<BT, NW>::BYTES;
     static constexpr int final_tile = PHASE == kFinal ? FinalLds<BT>::FLOATS * 4 : 0;
     static constexpr int value = main_loop > final_tile ? main_loop : final_tile;
 };
@@ -677,8 +610,8 @@ struct LdsBytes {
 template <typename T, int PHASE, int BT, int NW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uint8_t* lds_raw) {
     using S = Shape<BT, NW>;
-    using PP = Pipe<BT, NW, PipeFor<BT>::KSB, PipeFor<BT>::NBUF>;
-    constexpr int MM = S::MM, MN = S::MN, LP = PP::LP, KSB = PipeFor<BT>::KSB, NBUF = PipeFor<BT>::NBUF;
+    using PP = Pipe<BT, NW>;
+    constexpr int MM = S::MM, MN = S::MN, LP = PP::LP, KSB = PP::KSB;
     constexpr int SUBS = PP::SUBS, GR = PP::GR, OPB = PP::OPB;
     // the Gram's operands are K-major (X^T rows are the contraction index)
     constexpr bool KM = PHASE == kGram;
@@ -790,16 +723,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                 rs, (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]), 16, int(voff), u[i] + kt * step,
                 0, 0);
     };
-    auto issue = [&](int kt, int buf) {
-        const int kp = kt * stepP, kq = kt * stepQ;
-#pragma unroll
-        for (int i = 0; i < LP; ++i) {
-            auto* dstP = (__attribute__((address_space(3))) void*)(lds_raw + (2 * buf) * OPB + ldsd[i]);
-            auto* dstQ = (__attribute__((address_space(3))) void*)(lds_raw + (2 * buf + 1) * OPB + ldsd[i]);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, dstP, 16, int(voff), uP[i] + kp, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, dstQ, 16, int(voff), uQ[i] + kq, 0, 0);
-        }
-    };
 
     // Fragment of a 32-column MFMA tile starting at local column c of a
     // K-major tile: bf16, two transposing reads (k0..k0+3 and k0+4..k0+7);
@@ -857,10 +780,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
             for (int jj = 0; jj < MN; ++jj) bf[jj] = rowmajor_frag(oQ, wn * S::WTN + jj * 32 + frow, kk);
         }
-    };
-    // stage buffer b of the paired layout: P at (2b) * OPB, Q at (2b + 1) * OPB
-    auto frags = [&](int b, int kk, u32x4_t (&af)[MM], u32x4_t (&bf)[MN]) {
-        frags2(2 * b * OPB, (2 * b + 1) * OPB, kk, af, bf);
     };
     auto mfmas = [&](const u32x4_t (&af)[MM], const u32x4_t (&bf)[MN]) {
 #pragma unroll
@@ -1045,7 +964,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
         mfmas(fa1, fb1);  // last sub-step of the last stage
         wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
-    } else if constexpr (Ring32<T, PHASE, BT, NW>::value) {
+    } else {
         // Split rings: P's stage slots form a ring of 3 (byte offsets 0, OPB,
         // 2*OPB), Q's a ring of 2 (3*OPB, 4*OPB).  During stage t the block
         // loads Q of stage t + 1 and then P of stage t + 2, each into the slot
@@ -1092,109 +1011,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         }
         mfmas(fa1, fb1);  // last sub-step of the last stage
         wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
-    } else if constexpr (!PingPong<T, PHASE, BT, NW>::value) {
-        // Ring of NBUF stage buffers: stage t lives in buffer t % NBUF and its
-        // loads are issued NBUF - 1 stages ahead, into the buffer the previous
-        // stage has just released (every wave passed the barrier that ended it).
-        // A wave waits only for its own loads of the next stage (loads complete
-        // in issue order), then the barrier makes every wave's loads visible.
-        // Past the last stage the look-ahead re-loads the last stage into the
-        // released buffer, which no later stage reads: the loop has no branch and
-        // the wait count stays fixed.  Inside a stage, SUBS sub-steps of MM x MN
-        // MFMA steps with fragments double-buffered across sub-steps; the last
-        // sub-step's MFMAs (operands already in registers) run after the stage
-        // barrier, covering the LDS latency of the next stage's first fragments
-        // (the first deferred group multiplies zero fragments).
-        constexpr int D = NBUF - 1;                // look-ahead in stages
-        constexpr int VM_STAGE = 2 * LP;           // loads per wave and stage
-    #pragma unroll
-        for (int t = 0; t < D; ++t) issue(t < KT ? t : KT - 1, t);
-        wait_vmcnt<VM_STAGE * (D - 1)>();
-        stage_barrier();
-
-        u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
-    #pragma unroll
-        for (int i = 0; i < MM; ++i) fa1[i] = u32x4_t{0u, 0u, 0u, 0u};
-    #pragma unroll
-        for (int jj = 0; jj < MN; ++jj) fb1[jj] = u32x4_t{0u, 0u, 0u, 0u};
-        frags(0, 0, fa0, fb0);
-        int buf = 0;                 // buffer of stage kt
-        int lbuf = D;                // buffer receiving stage kt + D
-        for (int kt = 0; kt < KT; ++kt) {
-            issue(kt + D < KT ? kt + D : KT - 1, lbuf);
-            mfmas(fa1, fb1);  // last sub-step of the previous stage (zeros on the first)
-    #pragma unroll
-            for (int u = 1; u < SUBS; ++u) {
-                if (u & 1) {
-                    frags(buf, u, fa1, fb1);
-                    mfmas(fa0, fb0);  // sub-step u - 1
-                } else {
-                    frags(buf, u, fa0, fb0);
-                    mfmas(fa1, fb1);
-                }
-            }
-            if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), VM_STAGE, SUBS>();
-            wait_vmcnt<VM_STAGE * (D - 1)>();
-            stage_barrier();
-            buf = buf + 1 == NBUF ? 0 : buf + 1;
-            lbuf = lbuf + 1 == NBUF ? 0 : lbuf + 1;
-            frags(buf, 0, fa0, fb0);  // next stage's first fragments
-        }
-        mfmas(fa1, fb1);  // last sub-step of the last stage
-        wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
-    } else {
-        // Ping-pong.  Waves w and w + 4 share a SIMD (the hardware places a
-        // block's waves 0-3 on four different SIMDs and repeats that order for
-        // waves 4-7); group g = w / 4 thus holds one wave per SIMD.  The
-        // contraction runs in chunks of BURST sub-steps (CPS per stage) and in
-        // 2*NC + 1 phases separated by block barriers.  In phase p, group g
-        // reads every fragment of chunk (p - g)/2 from LDS into registers when
-        // p - g is even, and issues the MFMAs of the chunk it holds when p - g
-        // is odd: on each SIMD one wave multiplies back to back while the
-        // other fetches, and the roles swap every phase.  Stage s lives in
-        // buffer s % 2; all waves issue its direct-to-LDS loads in phase
-        // 2*CPS*(s - 1), once both groups have read stage s - 2 from that
-        // buffer, and wait for them at the end of phase 2*CPS*s - 1, before
-        // the barrier that lets group 0 read it.
-        constexpr int BURST = MFSDP_PP_BURST, CPS = SUBS / BURST;
-        static_assert(SUBS % BURST == 0, "burst");
-        const int g = wave_u >> 2;
-        const int NC = KT * CPS;
-        // the loads and waits that belong to phase p (same for every wave)
-        auto phase_loads = [&](int p) {
-            if (p % (2 * CPS) == 0 && p / (2 * CPS) + 1 < KT) issue(p / (2 * CPS) + 1, (p / (2 * CPS) + 1) & 1);
-        };
-        auto phase_end = [&](int p) {
-            if (p % (2 * CPS) == 2 * CPS - 1) wait_vmcnt<0>();
-            phase_barrier();
-        };
-        u32x4_t fa[BURST][MM], fb[BURST][MN];
-        issue(0, 0);
-        wait_vmcnt<0>();
-        __syncthreads();
-        // Every wave runs the same straight-line loop (fetch chunk c, then
-        // multiply it); group 1 runs it one phase later than group 0, so the
-        // accumulators never pass through a branch.
-        if (g == 1) {
-            phase_loads(0);
-            phase_end(0);
-        }
-        for (int c = 0; c < NC; ++c) {
-            const int p = 2 * c + g;
-            const int st = c / CPS, u0 = (c % CPS) * BURST;
-            phase_loads(p);
-#pragma unroll
-            for (int u = 0; u < BURST; ++u) frags(st & 1, u0 + u, fa[u], fb[u]);
-            phase_end(p);
-            phase_loads(p + 1);
-#pragma unroll
-            for (int u = 0; u < BURST; ++u) mfmas(fa[u], fb[u]);
-            phase_end(p + 1);
-        }
-        if (g == 0) {
-            phase_loads(2 * NC);
-            phase_end(2 * NC);
-        }
     }
 
     // ---- epilogue ----
@@ -1272,11 +1088,9 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
     gemm_tile<T, PHASE, BT, NW>(a, blockIdx.x, lds_raw);
 }
 
-// Wave count of the 256-tile kernels (4: one wave per SIMD with 128x128 each;
-// 8: two per SIMD with 128x64 each, measured faster).
-#ifndef MFSDP_WAVES_256
-#define MFSDP_WAVES_256 4
-#endif
+// 256 tiles: 4 waves, one per SIMD, 128 x 128 each (the locked schedule for
+// bf16); two waves per SIMD with 128 x 64 each measured 4-12% slower per
+// phase.  128 tiles: 4 waves of 64 x 64, two blocks per CU.
 
 template <typename T, int PHASE>
 void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
@@ -1284,8 +1098,7 @@ void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
     if (n_tiles <= 0) return;
     const int grid = n_tiles;
     if (tile == 256) {
-        constexpr int NW = MFSDP_WAVES_256;
-        k_ns_gemm<T, PHASE, 256, NW><<<dim3(grid), dim3(64 * NW), 0, stream>>>(a);
+        k_ns_gemm<T, PHASE, 256, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
     } else {
         k_ns_gemm<T, PHASE, 128, 4><<<dim3(grid), dim3(256), 0, stream>>>(a);
     }

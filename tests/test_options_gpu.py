@@ -61,8 +61,8 @@ def test_role_overrides():
 
 @pytest.mark.parametrize("precision", [0, 1])
 def test_ragged_shapes_on_256_tiles(precision, monkeypatch):
-    """Force the 256x256 tile kernels (for bf16: the ping-pong Gram and the
-    split-ring phases with 8 waves) onto shapes that are not multiples of
+    """Force the 256x256 tile kernels (for bf16: the locked 4-wave schedule
+    with the folded a X in the update phases) onto shapes that are not multiples of
     256, so their padding and the final update's bounds are exercised."""
     monkeypatch.setenv("MFSDP_TILE", "256")
     _steps(W.small_ragged(precision=precision), 2, label=f"t256-p{precision}")
