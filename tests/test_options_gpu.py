@@ -2,8 +2,9 @@
 not reach: Newton-Schulz step counts 0, 1 and 2 (no iteration: the update
 straight from the normalised input; the first iteration also being the
 last), the alternative learning-rate shape scale, plain (non-Nesterov)
-momentum, explicit role overrides, the 256-tile kernels on ragged shapes,
-and bitwise run-to-run determinism."""
+momentum, explicit role overrides, the 256-tile kernels on ragged shapes
+(also with other iteration coefficients), and bitwise run-to-run
+determinism."""
 
 import numpy as np
 import pytest
@@ -66,6 +67,17 @@ def test_ragged_shapes_on_256_tiles(precision, monkeypatch):
     256, so their padding and the final update's bounds are exercised."""
     monkeypatch.setenv("MFSDP_TILE", "256")
     _steps(W.small_ragged(precision=precision), 2, label=f"t256-p{precision}")
+
+
+@pytest.mark.parametrize("coeffs", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
+def test_other_coefficients_on_256_tiles(coeffs, monkeypatch):
+    """Other iteration coefficients on the 256-tile bf16 kernels (the cubic
+    iteration, c = 0, and a second quintic): the folded a X and the
+    polynomial's b A + c A^2 epilogue take the coefficients from the
+    parameters, and the oracle runs the same coefficients."""
+    monkeypatch.setenv("MFSDP_TILE", "256")
+    a, b, c = coeffs
+    _steps(W.small_ragged(precision=0), 1, {"ns_a": a, "ns_b": b, "ns_c": c}, label=f"coef{a},{b},{c}")
 
 
 def test_bitwise_deterministic():
