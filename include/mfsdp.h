@@ -168,12 +168,78 @@ mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsdp_entry_inf
  * kernel surfaces at the caller's next synchronisation.  One plan serves one
  * stream at a time; two steps that share a workspace must not overlap.
  * Errors: INVALID_ARGUMENT (null plan or args, null buffer needed by the
- * table, step < 1 with an AdamW entry, misaligned workspace),
- * too few events), WORKSPACE_TOO_SMALL, HIP. */
+ * table, step < 1 with an AdamW entry, misaligned workspace, too few
+ * events), WORKSPACE_TOO_SMALL, HIP. */
 mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args);
 
 /* Free a plan.  NULL is accepted. */
 mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
+
+/* ---- Owner planner (host only) ----
+ *
+ * "MatrixFSDP" (arXiv 2607.05895), Abstract: a balance-aware owner planner
+ * decides which data-parallel rank owns each whole 2D weight, and the
+ * non-matrix tensors are packed into tail owners.  The pages name the
+ * planner only; this one reads "balance-aware" as: every tensor goes whole
+ * to one owner, an owner's step time is the sum of its tensors' costs, and
+ * the plan minimises the largest owner time under a per-owner memory cap.
+ *
+ * Cost of a tensor: Muon (m = min(rows, cols), n = max): ns_steps * (4 m^2 n
+ * + 2 m^3) / flop_rate + rows*cols * (3 es + 8 + es_ns) / byte_rate (grad
+ * read, param read and write, fp32 momentum read and write, the
+ * Newton-Schulz input write; es = param bytes, es_ns = 2 for bf16
+ * Newton-Schulz, 4 for fp32); AdamW: rows*cols * (3 es + 16) / byte_rate.
+ * Memory of a tensor on its owner: params and grads (2 es per element),
+ * state (4 B per element for Muon, 8 for AdamW), and for Muon the
+ * Newton-Schulz buffers of mfsdp_plan_create (two X^T of n_p x m_p and A, B
+ * of m_p x m_p, m_p and n_p padded to 256, es_ns per element), each region
+ * rounded up to 256 bytes.  (The plan's descriptor blob and norm partials,
+ * a few bytes per tile, are not counted.)
+ *
+ * Algorithm: tensors in decreasing cost (ties: larger memory, then lower
+ * index) each go to the owner with the least cost so far that has room
+ * under the cap (ties: lower owner); then moves and swaps of single tensors
+ * off the most loaded owner are applied while they lower the largest owner
+ * cost.  Deterministic.  Without a binding cap the first pass alone is
+ * within 4/3 of the optimal largest cost (longest-processing-time bound).
+ */
+typedef struct mfsdp_tensor {
+    int64_t rows, cols;       /* 1D tensors: rows = 1; rows*cols = 0 is an empty tensor */
+    int32_t dtype;            /* mfsdp_dtype of params and grads */
+    int32_t role;             /* mfsdp_role, resolved as in mfsdp_entry */
+} mfsdp_tensor;
+
+typedef struct mfsdp_partition_params {
+    int32_t n_owners;         /* >= 1 */
+    int32_t ns_steps;         /* Newton-Schulz iterations in a Muon tensor's cost, >= 0 */
+    int32_t ns_precision;     /* 0: bf16 Newton-Schulz buffers, 1: fp32 */
+    int32_t reserved;         /* 0 */
+    uint64_t mem_cap_bytes;   /* per-owner memory cap; 0 = none */
+    double flop_rate;         /* FLOP/s of the Newton-Schulz contractions, > 0 */
+    double byte_rate;         /* bytes/s of the elementwise passes, > 0 */
+} mfsdp_partition_params;
+
+typedef struct mfsdp_tensor_place {
+    int32_t owner;            /* 0 .. n_owners-1 */
+    int32_t role;             /* resolved: MFSDP_ROLE_MUON or MFSDP_ROLE_ADAMW (empty tensors: ADAMW) */
+    uint64_t offset;          /* bytes into the owner's flat parameter buffer: the owner's tensors in
+                                 input order, each at a 256-byte aligned offset */
+    double cost;              /* seconds, by the model above */
+    uint64_t mem_bytes;       /* by the model above */
+} mfsdp_tensor_place;
+
+/* Assign n tensors to owners.  place: n entries, written on success.
+ * owner_cost, owner_mem_bytes, owner_param_bytes: NULL or n_owners entries
+ * each (sum of costs, sum of memory, end of the last tensor in the owner's
+ * flat buffer).  Each owner's tensors, in input order at their offsets, form
+ * a table mfsdp_plan_create accepts.
+ * Errors: INVALID_ARGUMENT (null pointer, n < 0, n_owners < 1, negative
+ * dimension, ns_steps < 0, rates not positive and finite), UNSUPPORTED
+ * (dtype, role, ns_precision, a tensor larger than the memory cap, or no
+ * owner with room left for a tensor). */
+mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64_t n, const mfsdp_partition_params* pp,
+                                   mfsdp_tensor_place* place, double* owner_cost, uint64_t* owner_mem_bytes,
+                                   uint64_t* owner_param_bytes);
 
 /* Static description of a status code. */
 const char* mfsdp_status_string(mfsdp_status status);

@@ -62,10 +62,25 @@ class StepArgs(ctypes.Structure):
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_uint32)]
 
 
+class Tensor(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("dtype", ctypes.c_int32), ("role", ctypes.c_int32)]
+
+
+class PartitionParams(ctypes.Structure):
+    _fields_ = [("n_owners", ctypes.c_int32), ("ns_steps", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("mem_cap_bytes", ctypes.c_uint64), ("flop_rate", ctypes.c_double),
+                ("byte_rate", ctypes.c_double)]
+
+
+class TensorPlace(ctypes.Structure):
+    _fields_ = [("owner", ctypes.c_int32), ("role", ctypes.c_int32), ("offset", ctypes.c_uint64),
+                ("cost", ctypes.c_double), ("mem_bytes", ctypes.c_uint64)]
+
+
 EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
     "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
-    "mfsdp_status_string", "mfsdp_last_error_message",
+    "mfsdp_owner_partition", "mfsdp_status_string", "mfsdp_last_error_message",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -91,6 +106,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_plan_entry_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(EntryInfo)]
     lib.mfsdp_owner_step.argtypes = [P, ctypes.POINTER(StepArgs)]
     lib.mfsdp_plan_destroy.argtypes = [P]
+    lib.mfsdp_owner_partition.argtypes = [ctypes.POINTER(Tensor), ctypes.c_int64, ctypes.POINTER(PartitionParams),
+                                          ctypes.POINTER(TensorPlace), ctypes.POINTER(ctypes.c_double), u64p, u64p]
     lib.mfsdp_status_string.argtypes = [ctypes.c_int]
     lib.mfsdp_status_string.restype = ctypes.c_char_p
     lib.mfsdp_last_error_message.argtypes = []
@@ -201,3 +218,45 @@ class OwnerPlan:
             self.close()
         except Exception:
             pass
+
+
+@dataclass(frozen=True)
+class Partition:
+    """Result of owner_partition: per tensor its owner, resolved role and
+    byte offset in that owner's flat parameter buffer, and its model cost and
+    memory; per owner the summed cost, memory and parameter bytes."""
+    owner: list
+    role: list
+    offset: list
+    cost: list
+    mem_bytes: list
+    owner_cost: list
+    owner_mem_bytes: list
+    owner_param_bytes: list
+
+    def table(self, o: int, dtypes: Sequence[int], shapes: Sequence[tuple]) -> list:
+        """Owner o's table (input order) as TableEntry rows."""
+        return [TableEntry(self.offset[i], shapes[i][0], shapes[i][1], dtypes[i], self.role[i])
+                for i in range(len(self.owner)) if self.owner[i] == o]
+
+
+def owner_partition(shapes: Sequence[tuple], dtypes: Sequence[int], n_owners: int, *, roles: Sequence[int] = None,
+                    ns_steps: int = 5, ns_precision: int = 0, mem_cap_bytes: int = 0, flop_rate: float = 1.6e15,
+                    byte_rate: float = 5.2e12) -> Partition:
+    """Balance-aware assignment of whole tensors to owners (mfsdp_owner_partition)."""
+    lib = load()
+    n = len(shapes)
+    roles = list(roles) if roles is not None else [ROLE_AUTO] * n
+    arr = (Tensor * max(n, 1))(*[Tensor(int(r), int(c), int(dt), int(ro))
+                                 for (r, c), dt, ro in zip(shapes, dtypes, roles)])
+    pp = PartitionParams(int(n_owners), int(ns_steps), int(ns_precision), 0, int(mem_cap_bytes), float(flop_rate),
+                         float(byte_rate))
+    place = (TensorPlace * max(n, 1))()
+    oc = (ctypes.c_double * max(int(n_owners), 1))()
+    om = (ctypes.c_uint64 * max(int(n_owners), 1))()
+    ob = (ctypes.c_uint64 * max(int(n_owners), 1))()
+    _check(lib.mfsdp_owner_partition(arr, n, ctypes.byref(pp), place, oc, om, ob))
+    return Partition([place[i].owner for i in range(n)], [place[i].role for i in range(n)],
+                     [place[i].offset for i in range(n)], [place[i].cost for i in range(n)],
+                     [place[i].mem_bytes for i in range(n)], list(oc[:n_owners]), list(om[:n_owners]),
+                     list(ob[:n_owners]))

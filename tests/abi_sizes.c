@@ -26,5 +26,14 @@ int main(void) {
     OF(mfsdp_step_args, params); OF(mfsdp_step_args, grads); OF(mfsdp_step_args, state); OF(mfsdp_step_args, workspace);
     OF(mfsdp_step_args, workspace_bytes); OF(mfsdp_step_args, step); OF(mfsdp_step_args, stream);
     OF(mfsdp_step_args, ns_out); OF(mfsdp_step_args, flags); OF(mfsdp_step_args, events); OF(mfsdp_step_args, n_events);
+    SZ(mfsdp_tensor);
+    OF(mfsdp_tensor, rows); OF(mfsdp_tensor, cols); OF(mfsdp_tensor, dtype); OF(mfsdp_tensor, role);
+    SZ(mfsdp_partition_params);
+    OF(mfsdp_partition_params, n_owners); OF(mfsdp_partition_params, ns_steps); OF(mfsdp_partition_params, ns_precision);
+    OF(mfsdp_partition_params, reserved); OF(mfsdp_partition_params, mem_cap_bytes);
+    OF(mfsdp_partition_params, flop_rate); OF(mfsdp_partition_params, byte_rate);
+    SZ(mfsdp_tensor_place);
+    OF(mfsdp_tensor_place, owner); OF(mfsdp_tensor_place, role); OF(mfsdp_tensor_place, offset);
+    OF(mfsdp_tensor_place, cost); OF(mfsdp_tensor_place, mem_bytes);
     return 0;
 }

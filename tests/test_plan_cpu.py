@@ -47,7 +47,8 @@ def test_struct_layouts_match_header(tmp_path):
                     "-o", exe], check=True)
     out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     mirrors = {"mfsdp_entry": B.Entry, "mfsdp_hparams": B.Hparams, "mfsdp_entry_info": B.EntryInfo,
-               "mfsdp_step_args": B.StepArgs}
+               "mfsdp_step_args": B.StepArgs, "mfsdp_tensor": B.Tensor, "mfsdp_partition_params": B.PartitionParams,
+               "mfsdp_tensor_place": B.TensorPlace}
     checked = 0
     for line in filter(None, out):
         key, val = line.split()
