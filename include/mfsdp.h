@@ -241,6 +241,34 @@ mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64_t n, const
                                    mfsdp_tensor_place* place, double* owner_cost, uint64_t* owner_mem_bytes,
                                    uint64_t* owner_param_bytes);
 
+/* ---- Owner-shard checkpoint resharding (host only) ----
+ *
+ * "MatrixFSDP" (arXiv 2607.05895), Abstract: owner-shard checkpoint
+ * resharding.  A checkpoint holds whole tensors; these two calls copy one
+ * owner's tensors and their optimizer state between the owner's flat
+ * buffers (laid out by its plan) and one buffer per tensor, in host memory,
+ * byte for byte (no conversion).  Resharding to another owner count is
+ * gather from every old owner, mfsdp_owner_partition for the new count,
+ * scatter into every new owner; every value comes back bit-exact.
+ *
+ * For entry i of the plan's table (numel = rows*cols):
+ *   tensors[i]  numel parameter elements in the entry's dtype, row-major;
+ *   state1[i]   numel fp32: Muon momentum, or AdamW first moment;
+ *   state2[i]   numel fp32: AdamW second moment (unused for Muon).
+ * Any array pointer may be NULL (that part is not copied); an element may be
+ * NULL where numel is 0 or the part does not apply.  params / state are the
+ * owner's buffers (param_bytes >= the end of its last tensor, state_bytes >=
+ * mfsdp_plan_state_bytes).  Bytes outside the tensors and state regions are
+ * not touched.
+ * Errors: INVALID_ARGUMENT (null plan, a needed buffer or element NULL,
+ * buffer too small). */
+mfsdp_status mfsdp_owner_gather(mfsdp_plan_t plan, const void* params, uint64_t param_bytes, const void* state,
+                                uint64_t state_bytes, void* const* tensors, void* const* state1,
+                                void* const* state2);
+mfsdp_status mfsdp_owner_scatter(mfsdp_plan_t plan, const void* const* tensors, const void* const* state1,
+                                 const void* const* state2, void* params, uint64_t param_bytes, void* state,
+                                 uint64_t state_bytes);
+
 /* Static description of a status code. */
 const char* mfsdp_status_string(mfsdp_status status);
 

@@ -80,7 +80,8 @@ class TensorPlace(ctypes.Structure):
 EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
     "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
-    "mfsdp_owner_partition", "mfsdp_status_string", "mfsdp_last_error_message",
+    "mfsdp_owner_partition", "mfsdp_owner_gather", "mfsdp_owner_scatter", "mfsdp_status_string",
+    "mfsdp_last_error_message",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -108,6 +109,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_plan_destroy.argtypes = [P]
     lib.mfsdp_owner_partition.argtypes = [ctypes.POINTER(Tensor), ctypes.c_int64, ctypes.POINTER(PartitionParams),
                                           ctypes.POINTER(TensorPlace), ctypes.POINTER(ctypes.c_double), u64p, u64p]
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.mfsdp_owner_gather.argtypes = [P, P, ctypes.c_uint64, P, ctypes.c_uint64, vpp, vpp, vpp]
+    lib.mfsdp_owner_scatter.argtypes = [P, vpp, vpp, vpp, P, ctypes.c_uint64, P, ctypes.c_uint64]
     lib.mfsdp_status_string.argtypes = [ctypes.c_int]
     lib.mfsdp_status_string.restype = ctypes.c_char_p
     lib.mfsdp_last_error_message.argtypes = []
@@ -207,6 +211,26 @@ class OwnerPlan:
         args = StepArgs(params, grads, state, workspace, workspace_bytes, step, stream or None, ns_out or None, flags,
                         ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None, len(events))
         _check(self._lib.mfsdp_owner_step(self._h, ctypes.byref(args)))
+
+    def _ptrs(self, addrs):
+        if addrs is None:
+            return None
+        if len(addrs) != self.n_entries:
+            raise ValueError(f"{len(addrs)} buffers for {self.n_entries} entries")
+        return (ctypes.c_void_p * max(1, self.n_entries))(*[a or None for a in addrs])
+
+    def gather(self, params: int, param_bytes: int, state: int, state_bytes: int, tensors=None, state1=None,
+               state2=None) -> None:
+        """Copy the owner's tensors and state (host buffers at the given
+        addresses) out to one host buffer per entry (lists of addresses,
+        0 for none; a list may be None)."""
+        _check(self._lib.mfsdp_owner_gather(self._h, params or None, param_bytes, state or None, state_bytes,
+                                            self._ptrs(tensors), self._ptrs(state1), self._ptrs(state2)))
+
+    def scatter(self, tensors, state1, state2, params: int, param_bytes: int, state: int, state_bytes: int) -> None:
+        """Copy per-entry host buffers into the owner's flat host buffers."""
+        _check(self._lib.mfsdp_owner_scatter(self._h, self._ptrs(tensors), self._ptrs(state1), self._ptrs(state2),
+                                             params or None, param_bytes, state or None, state_bytes))
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
