@@ -166,9 +166,20 @@ def _table_text(wl):
     return "\n".join(lines) + "\n"
 
 
-@pytest.mark.parametrize("name", ["small_ragged", "c0", "c1", "c2", "c3", "c4"])
+def _max_size(rows, cols):
+    """The largest ragged matrices the planner accepts (padded 32512 x 32768)."""
+    return W.Workload(f"max-{rows}x{cols}", [W.TensorSpec("w", rows, cols)], seed=6,
+                      hparams=dict(W.MUON_DEFAULTS, ns_precision=0))
+
+
+@pytest.mark.parametrize("name", ["small_ragged", "c0", "c1", "c2", "c3", "c4", "max_wide", "max_tall"])
 def test_plan_descriptor_invariants(plan_checker, name):
-    wl = W.small_ragged() if name == "small_ragged" else W.config(int(name[1]))
+    if name == "small_ragged":
+        wl = W.small_ragged()
+    elif name.startswith("max_"):
+        wl = _max_size(32500, 32700) if name == "max_wide" else _max_size(32700, 32500)
+    else:
+        wl = W.config(int(name[1]))
     res = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.startswith("OK"), res.stdout
