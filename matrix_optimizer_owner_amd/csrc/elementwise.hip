@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_final_from_x(FinalArgs a) {
     const int tr = local / d.k1_tiles_c, tc = local % d.k1_tiles_c;
     const T* xt0 = reinterpret_cast<const T*>(a.ws + d.x_off[0]);
     const float s = a.s[mi];
-    const float step = a.lr * d.lr_scale;
+    const float step = d.lr_step;
     uint8_t* w = a.params + d.param_off;
     for (int e = threadIdx.x; e < kK1Tile * kK1Tile; e += 256) {
         const int r = tr * kK1Tile + e / kK1Tile, c = tc * kK1Tile + e % kK1Tile;

@@ -53,7 +53,7 @@ struct MatDesc {
     int32_t mp, np;        // padded to kPad
     int32_t transposed;    // rows > cols
     int32_t dtype;         // param / grad storage type
-    float lr_scale;        // shape scale of the learning rate
+    float lr_step;         // lr * shape scale of the learning rate, rounded once to fp32
     int32_t k1_tiles_c;    // momentum-kernel tile columns (natural layout)
 };
 

@@ -288,7 +288,7 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
     constexpr int PFB = sizeof(T) == 2 ? 256 : 128;  // prefetch bytes per lane (fp32 X^T needs more registers)
     constexpr int PF = NPT * int(sizeof(Raw)) <= PFB ? NPT : PFB / int(sizeof(Raw));  // chunks per batch
     static_assert(CHUNKS % S::kThreads == 0 && NPT % PF == 0, "walk");
-    const float step = a.lr * d.lr_scale;
+    const float step = d.lr_step;
     const uint32_t ld = uint32_t(d.ld);  // row pitch of X^T
     const int ldw = d.cols;
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;

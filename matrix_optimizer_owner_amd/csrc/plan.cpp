@@ -54,9 +54,9 @@ mfsdp_status check_hparams(const mfsdp_hparams& hp) {
     return MFSDP_OK;
 }
 
-float shape_scale(int64_t rows, int64_t cols, int mode) {
-    if (mode == 0) return float(std::sqrt(std::max(1.0, double(rows) / double(cols))));
-    return float(0.2 * std::sqrt(double(std::max(rows, cols))));
+double shape_scale(int64_t rows, int64_t cols, int mode) {
+    if (mode == 0) return std::sqrt(std::max(1.0, double(rows) / double(cols)));
+    return 0.2 * std::sqrt(double(std::max(rows, cols)));
 }
 
 // Tiles of one matrix for one phase in 2D chunks of kChunkRows x kChunkCols
@@ -161,7 +161,7 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
                 inf.transposed = e.rows > e.cols ? 1 : 0;
                 inf.m = std::min(e.rows, e.cols);
                 inf.n = std::max(e.rows, e.cols);
-                inf.lr_scale = shape_scale(e.rows, e.cols, hp->lr_scale_mode);
+                inf.lr_scale = float(shape_scale(e.rows, e.cols, hp->lr_scale_mode));
             }
         }
         std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
@@ -222,7 +222,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             }
             d.transposed = inf.transposed;
             d.dtype = e.dtype;
-            d.lr_scale = inf.lr_scale;
+            // the kernels' step lr * scale, rounded once to fp32
+            d.lr_step = float(double(hp->lr) * shape_scale(e.rows, e.cols, hp->lr_scale_mode));
             const int ncols_nat = inf.transposed ? d.mp : d.np;  // padded natural column count
             d.k1_tiles_c = ncols_nat / kK1Tile;
             inf.ns_out_offset = ns_off;

@@ -73,7 +73,7 @@ int main() {
         CHECK(d.mp % kPad == 0 && d.np % kPad == 0 && d.mp >= d.m && d.np >= d.n && d.mp - d.m < kPad &&
                   d.np - d.n < kPad, "entry %lld padding", i);
         const double want = std::sqrt(std::max(1.0, double(e.rows) / double(e.cols)));
-        CHECK(std::fabs(d.lr_scale - float(want)) == 0.0f, "entry %lld lr scale %g vs %g", i, d.lr_scale, want);
+        CHECK(d.lr_step == float(double(hp.lr) * want), "entry %lld lr step %g vs %g", i, d.lr_step, double(hp.lr) * want);
         CHECK(d.mom_off == inf.state_offset && d.mom_off % kAlign == 0, "entry %lld momentum offset", i);
     }
     CHECK(mi == w.n_mat, "matrix count %d vs %d", mi, w.n_mat);

@@ -67,7 +67,7 @@ def check_elementwise(run, snap, i, hp, rng, samples=4096):
     assert np.max(np.abs(m1[idx] - m_orc)) <= 1e-6 * max(np.max(np.abs(m_orc)), 1e-30)
     w_ref = orc.round_to_dtype(orc.apply_update(snap[(i, "param")][idx], o[idx], s.rows, s.cols, hp), s.dtype)
     step_term = np.abs(hp.lr * orc.lr_shape_scale(s.rows, s.cols, hp.lr_scale_mode) * o[idx])
-    tol = ulp(w_ref, s.dtype) + ulp(np.maximum(np.abs(snap[(i, "param")][idx]), step_term), "f32")
+    tol = ulp(w_ref, s.dtype) + ulp(snap[(i, "param")][idx], "f32") + ulp(step_term, "f32")
     assert np.max(np.abs(w1[idx] - w_ref) / tol) <= 1.0
     return o
 
