@@ -10,7 +10,8 @@ synthetic and resident in HBM before the timed region.  Prints ONE JSON line.
 
 --config selects the workload (0 single 256x512 fp32, 1 GPT-2-small owner
 buffer, 2 Llama-3-8B owner share (default), 3 mixed 256-matrix stress,
-4 Llama-3-70B owner share).  --copy-probe-gib G instead runs a plain device
+4 Llama-3-70B owner share, 5 a tail-only buffer of 268 M fp32 elements that
+measures the AdamW kernel against HBM bandwidth).  --copy-probe-gib G instead runs a plain device
 copy of G GiB (used to scale the HBM byte counters of rocprofv3).
 """
 
@@ -90,6 +91,8 @@ def cpu_baseline(wl, budget_s: float):
     hp = orc.Hparams(ns_steps=int(wl.hparams.get("ns_steps", 5)))
     specs = wl.muon_specs()
     steps = hp.ns_steps
+    if not specs:
+        return cpu_baseline_tail(wl, hp, budget_s, cores)
 
     def flops(s):
         m, n = min(s.rows, s.cols), max(s.rows, s.cols)
@@ -131,6 +134,32 @@ def cpu_baseline(wl, budget_s: float):
                    f"to the whole owner step ({total / 1e12:.2f} TFLOP)"),
         "tflops_fp64": f_used / t_used / 1e12 if t_used else None,
     }
+
+
+def cpu_baseline_tail(wl, hp, budget_s: float, cores: int):
+    """The fp64 oracle's AdamW step on as many tail tensors as fit the budget,
+    extrapolated to the whole tail by element count."""
+    import numpy as np
+
+    from oracle import muon_oracle as orc
+
+    rng = np.random.default_rng(0)
+    t_used, el_used, n = 0.0, 0, 0
+    total = sum(s.numel for s in wl.specs)
+    for s in wl.specs:
+        if t_used > budget_s:
+            break
+        w = np.ones(s.numel)
+        g = rng.standard_normal(s.numel) * s.grad_std
+        z = np.zeros(s.numel)
+        t0 = time.perf_counter()
+        orc.adamw_step(w, g, z, z, 1, hp)
+        t_used += time.perf_counter() - t0
+        el_used += s.numel
+        n += 1
+    return {"value": t_used * total / el_used * 1e3, "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle AdamW step on {n} of {len(wl.specs)} tail tensors ({el_used} elements, "
+                      f"{t_used:.1f} s), extrapolated by element count to the whole tail ({total} elements)"}
 
 
 # HBM bytes per launch of the dominant kernel, from rocprofv3 counter runs
@@ -260,12 +289,14 @@ def main() -> int:
     upd_f = gram_f
     per_launch = {"gram": gram_f, "poly": poly_f, "update": upd_f, "final": upd_f}
     tot = {k: sum(ph[k]) for k in per_launch}
-    dom = max(tot, key=tot.get) if steps_ns else None
+    dom = max(tot, key=tot.get) if steps_ns and specs else None
     peak = PEAK_TFLOPS[prec]
     ns_ms = mean(ph["ns"])
     nominal = wl.nominal_ns_flops()
     muon_el = wl.muon_elements()
     tail_el = sum(s.numel for s in wl.specs if s not in specs and s.numel > 0)
+    # AdamW moves W, g (storage type), m and v (fp32) in and W, m, v out
+    tail_bytes = sum(s.numel * (3 * s.itemsize + 16) for s in wl.specs if s not in specs and s.numel > 0)
     k1_bytes = muon_el * (12 if prec == "bf16" else 16)
     mom_ms = mean(ph["momentum"])
     adam_ms = mean(ph["adamw"])
@@ -300,6 +331,12 @@ def main() -> int:
     del cbuf, csrc, cdst
 
     roofline = None
+    if not specs and adam_ms:
+        # tail-only buffer: the AdamW kernel is the step (28 B per fp32 element)
+        ach = tail_bytes / (adam_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "k_adamw",
+                    "avg_launch_ms": round(adam_ms, 4), "algorithmic_bytes_per_launch": tail_bytes}
     if dom:
         avg = mean(ph[dom])
         ach = per_launch[dom] / (avg * 1e-3) / 1e12
@@ -319,7 +356,7 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": prec,
+        "dtype": prec if specs else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "muon_matrices": len(specs), "muon_elements": muon_el,
                    "tail_tensors": sum(1 for s in wl.specs if s not in specs and s.numel > 0),
@@ -340,7 +377,7 @@ def main() -> int:
                         "momentum_bytes_per_elem": 12 if prec == "bf16" else 16,
                         "copy_ceiling_gbs": round(copy_gbs, 1),
                         "momentum_frac_copy_ceiling": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / copy_gbs, 4) if mom_ms else None,
-                        "adamw_gbs": round(28 * tail_el / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},
+                        "adamw_gbs": round(tail_bytes / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -169,7 +169,16 @@ def llama3_70b_share() -> Workload:
     return Workload("llama3-70b-owner-share-2L", sp, seed=4, hparams=dict(MUON_DEFAULTS, ns_precision=0))
 
 
-CONFIGS = [single_fp32, gpt2_small, llama3_8b_share, mixed_stress, llama3_70b_share]
+def adamw_tail_probe() -> Workload:
+    """Tail-only owner buffer for measuring the AdamW kernel where HBM bounds
+    it: 64 fp32 vectors of 4 Mi elements (268 M elements, 7.5 GB moved per
+    step).  Not one of the five workloads; the GPT-2 tail (121,344
+    elements) is too small for its time to say anything about bandwidth."""
+    sp = [TensorSpec(f"tail{i}", 1, 4 << 20, "f32", "zeros" if i % 2 else "ones", grad_std=1e-3) for i in range(64)]
+    return Workload("adamw-tail-64x4Mi-fp32", sp, seed=7, hparams=dict(MUON_DEFAULTS, ns_precision=0))
+
+
+CONFIGS = [single_fp32, gpt2_small, llama3_8b_share, mixed_stress, llama3_70b_share, adamw_tail_probe]
 
 
 def config(i: int) -> Workload:
