@@ -201,6 +201,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0)
+    ap.add_argument("--momentum-dtype", choices=("f32", "bf16"), default="f32",
+                    help="storage type of the Muon momentum (the workloads state fp32)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -221,7 +223,7 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     wl = W.config(args.config)
-    hp = dict(wl.hparams)
+    hp = dict(wl.hparams, momentum_dtype=B.BF16 if args.momentum_dtype == "bf16" else B.F32)
     prec = "fp32" if int(hp.get("ns_precision", 0)) == 1 else "bf16"
     offs, pbytes = wl.layout()
     dt = {"bf16": B.BF16, "f32": B.F32}
@@ -297,7 +299,10 @@ def main() -> int:
     tail_el = sum(s.numel for s in wl.specs if s not in specs and s.numel > 0)
     # AdamW moves W, g (storage type), m and v (fp32) in and W, m, v out
     tail_bytes = sum(s.numel * (3 * s.itemsize + 16) for s in wl.specs if s not in specs and s.numel > 0)
-    k1_bytes = muon_el * (12 if prec == "bf16" else 16)
+    # momentum pass: g read, momentum read and written, X0 written
+    em = 2 if args.momentum_dtype == "bf16" else 4
+    es_ns = 2 if prec == "bf16" else 4
+    k1_bytes = sum(s.numel * (s.itemsize + 2 * em + es_ns) for s in specs)
     mom_ms = mean(ph["momentum"])
     adam_ms = mean(ph["adamw"])
 
@@ -360,7 +365,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "muon_matrices": len(specs), "muon_elements": muon_el,
                    "tail_tensors": sum(1 for s in wl.specs if s not in specs and s.numel > 0),
-                   "tail_elements": tail_el, "ns_steps": steps_ns, "parallelism": "single GPU owner"},
+                   "tail_elements": tail_el, "ns_steps": steps_ns, "momentum_dtype": args.momentum_dtype,
+                   "parallelism": "single GPU owner"},
         "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
         "step_ms_p90": round(sorted(step_ms)[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4),
         "step_ms_all": [round(x, 4) for x in step_ms],
@@ -374,7 +380,7 @@ def main() -> int:
                       "update_avg": round(mean(ph["update"]), 4), "final_update": round(mean(ph["final"]), 4)},
         "elementwise": {"momentum_gbs": round(k1_bytes / (mom_ms * 1e-3) / 1e9, 1) if mom_ms else None,
                         "momentum_frac_hbm": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if mom_ms else None,
-                        "momentum_bytes_per_elem": 12 if prec == "bf16" else 16,
+                        "momentum_bytes_per_elem": round(k1_bytes / muon_el, 3) if muon_el else None,
                         "copy_ceiling_gbs": round(copy_gbs, 1),
                         "momentum_frac_copy_ceiling": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / copy_gbs, 4) if mom_ms else None,
                         "adamw_gbs": round(tail_bytes / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},

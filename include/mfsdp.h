@@ -94,6 +94,12 @@ typedef struct mfsdp_hparams {
     float adam_beta2;
     float adam_eps;
     float adam_weight_decay;
+    int32_t momentum_dtype;   /* storage type of the Muon momentum: MFSDP_F32 (0, the default) or
+                                 MFSDP_BF16, rounded to nearest-even once per step.  bf16 halves the
+                                 momentum's memory, keeping the owner's optimizer state small (the
+                                 ZeRO-3-scale memory the MatrixFSDP abstract asks for), and the
+                                 momentum pass then moves 8 B per bf16 element instead of 12.  The
+                                 AdamW moments stay fp32. */
 } mfsdp_hparams;
 
 typedef struct mfsdp_plan_s* mfsdp_plan_t;
@@ -103,7 +109,7 @@ typedef struct mfsdp_entry_info {
     int32_t role;             /* resolved: MFSDP_ROLE_MUON, MFSDP_ROLE_ADAMW, or -1 for an empty entry */
     int32_t transposed;       /* Muon: 1 if rows > cols (Newton-Schulz runs on the transpose) */
     int64_t m, n;             /* Muon: oriented shape, m = min(rows, cols) */
-    uint64_t state_offset;    /* Muon: fp32 momentum; AdamW: fp32 first moment (bytes into state) */
+    uint64_t state_offset;    /* Muon: momentum (momentum_dtype); AdamW: fp32 first moment (bytes into state) */
     uint64_t state_offset2;   /* AdamW: fp32 second moment (bytes into state); 0 otherwise */
     uint64_t ns_out_offset;   /* Muon: element offset of the fp32 O export in ns_out */
     float lr_scale;           /* Muon: the shape scale applied to lr */
@@ -185,12 +191,13 @@ mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
  * the plan minimises the largest owner time under a per-owner memory cap.
  *
  * Cost of a tensor: Muon (m = min(rows, cols), n = max): ns_steps * (4 m^2 n
- * + 2 m^3) / flop_rate + rows*cols * (3 es + 8 + es_ns) / byte_rate (grad
- * read, param read and write, fp32 momentum read and write, the
- * Newton-Schulz input write; es = param bytes, es_ns = 2 for bf16
- * Newton-Schulz, 4 for fp32); AdamW: rows*cols * (3 es + 16) / byte_rate.
+ * + 2 m^3) / flop_rate + rows*cols * (3 es + 2 em + es_ns) / byte_rate (grad
+ * read, param read and write, momentum read and write, the Newton-Schulz
+ * input write; es = param bytes, em = momentum bytes (4, or 2 with
+ * momentum_dtype MFSDP_BF16), es_ns = 2 for bf16 Newton-Schulz, 4 for fp32);
+ * AdamW: rows*cols * (3 es + 16) / byte_rate.
  * Memory of a tensor on its owner: params and grads (2 es per element),
- * state (4 B per element for Muon, 8 for AdamW), and for Muon the
+ * state (em B per element for Muon, 8 for AdamW), and for Muon the
  * Newton-Schulz buffers of mfsdp_plan_create (two X^T of n_p x m_p and A, B
  * of m_p x m_p, m_p and n_p padded to 256, es_ns per element), each region
  * rounded up to 256 bytes.  (The plan's descriptor blob and norm partials,
@@ -213,7 +220,7 @@ typedef struct mfsdp_partition_params {
     int32_t n_owners;         /* >= 1 */
     int32_t ns_steps;         /* Newton-Schulz iterations in a Muon tensor's cost, >= 0 */
     int32_t ns_precision;     /* 0: bf16 Newton-Schulz buffers, 1: fp32 */
-    int32_t reserved;         /* 0 */
+    int32_t momentum_dtype;   /* Muon momentum storage, as in mfsdp_hparams: MFSDP_F32 (0) or MFSDP_BF16 */
     uint64_t mem_cap_bytes;   /* per-owner memory cap; 0 = none */
     double flop_rate;         /* FLOP/s of the Newton-Schulz contractions, > 0 */
     double byte_rate;         /* bytes/s of the elementwise passes, > 0 */
@@ -253,7 +260,7 @@ mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64_t n, const
  *
  * For entry i of the plan's table (numel = rows*cols):
  *   tensors[i]  numel parameter elements in the entry's dtype, row-major;
- *   state1[i]   numel fp32: Muon momentum, or AdamW first moment;
+ *   state1[i]   numel elements: Muon momentum (the plan's momentum_dtype), or AdamW first moment (fp32);
  *   state2[i]   numel fp32: AdamW second moment (unused for Muon).
  * Any array pointer may be NULL (that part is not copied); an element may be
  * NULL where numel is 0 or the part does not apply.  params / state are the

@@ -46,6 +46,7 @@ class Hparams(ctypes.Structure):
         ("lr_scale_mode", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
         ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
         ("adam_eps", ctypes.c_float), ("adam_weight_decay", ctypes.c_float),
+        ("momentum_dtype", ctypes.c_int32),
     ]
 
 
@@ -68,7 +69,7 @@ class Tensor(ctypes.Structure):
 
 class PartitionParams(ctypes.Structure):
     _fields_ = [("n_owners", ctypes.c_int32), ("ns_steps", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("mem_cap_bytes", ctypes.c_uint64), ("flop_rate", ctypes.c_double),
+                ("momentum_dtype", ctypes.c_int32), ("mem_cap_bytes", ctypes.c_uint64), ("flop_rate", ctypes.c_double),
                 ("byte_rate", ctypes.c_double)]
 
 
@@ -140,12 +141,12 @@ def make_hparams(**kw) -> Hparams:
     """Hyper-parameters with Muon/AdamW defaults; keyword overrides."""
     d = dict(lr=0.02, weight_decay=0.01, momentum=0.95, nesterov=1, ns_steps=5, ns_a=3.4445, ns_b=-4.7750,
              ns_c=2.0315, ns_eps=1e-7, lr_scale_mode=0, ns_precision=0, adam_lr=0.02, adam_beta1=0.9,
-             adam_beta2=0.95, adam_eps=1e-8, adam_weight_decay=0.01)
+             adam_beta2=0.95, adam_eps=1e-8, adam_weight_decay=0.01, momentum_dtype=0)
     unknown = set(kw) - set(d)
     if unknown:
         raise KeyError(f"unknown hyper-parameters {sorted(unknown)}")
     d.update(kw)
-    ints = {"nesterov", "ns_steps", "lr_scale_mode", "ns_precision"}
+    ints = {"nesterov", "ns_steps", "lr_scale_mode", "ns_precision", "momentum_dtype"}
     return Hparams(**{k: (int(v) if k in ints else float(v)) for k, v in d.items()})
 
 
@@ -266,14 +267,15 @@ class Partition:
 
 def owner_partition(shapes: Sequence[tuple], dtypes: Sequence[int], n_owners: int, *, roles: Sequence[int] = None,
                     ns_steps: int = 5, ns_precision: int = 0, mem_cap_bytes: int = 0, flop_rate: float = 1.6e15,
-                    byte_rate: float = 5.2e12) -> Partition:
+                    byte_rate: float = 5.2e12, momentum_dtype: int = 0) -> Partition:
     """Balance-aware assignment of whole tensors to owners (mfsdp_owner_partition)."""
     lib = load()
     n = len(shapes)
     roles = list(roles) if roles is not None else [ROLE_AUTO] * n
     arr = (Tensor * max(n, 1))(*[Tensor(int(r), int(c), int(dt), int(ro))
                                  for (r, c), dt, ro in zip(shapes, dtypes, roles)])
-    pp = PartitionParams(int(n_owners), int(ns_steps), int(ns_precision), 0, int(mem_cap_bytes), float(flop_rate),
+    pp = PartitionParams(int(n_owners), int(ns_steps), int(ns_precision), int(momentum_dtype), int(mem_cap_bytes),
+                         float(flop_rate),
                          float(byte_rate))
     place = (TensorPlace * max(n, 1))()
     oc = (ctypes.c_double * max(int(n_owners), 1))()

@@ -38,7 +38,9 @@ mfsdp_status walk(mfsdp_plan_t plan, uint64_t param_bytes, uint64_t state_bytes,
             if (st != MFSDP_OK) return st;
         }
         if (want_s1) {
-            const mfsdp_status st = copy(i, 1, inf.state_offset, numel * 4);
+            const uint64_t s1_bytes =
+                inf.role == MFSDP_ROLE_MUON && plan->hp.momentum_dtype == MFSDP_BF16 ? 2 : 4;
+            const mfsdp_status st = copy(i, 1, inf.state_offset, numel * s1_bytes);
             if (st != MFSDP_OK) return st;
         }
         if (want_s2 && inf.role == MFSDP_ROLE_ADAMW) {

@@ -30,7 +30,34 @@ struct MomentumArgs {
     int nesterov;
 };
 
-template <typename T> struct Vec8;  // eight elements of the Newton-Schulz storage type
+// Eight consecutive momentum elements (fp32, or bf16 bits in uint16_t):
+// one raw vector load, unpacked to fp32.
+template <typename MT> struct Mom8;
+template <> struct Mom8<float> {
+    struct raw { float4 a, b; };
+    __device__ static raw load(const float* p) {
+        const float4* q = reinterpret_cast<const float4*>(p);
+        return raw{q[0], q[1]};
+    }
+    __device__ static void get(const raw& r, float (&v)[8]) {
+        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+    }
+};
+template <> struct Mom8<uint16_t> {
+    using raw = uint4;
+    __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+    __device__ static void get(const raw& r, float (&v)[8]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+};
+
+template <typename T> struct Vec8;  // eight elements of the Newton-Schulz (or momentum) storage type
 template <> struct Vec8<uint16_t> {
     __device__ static void store(uint16_t* p, const float* u) {
         uint4 v;
@@ -54,8 +81,10 @@ template <> struct Vec8<float> {
 // registers, then 8 stores of 8 elements to X0^T - along the natural rows for
 // a tall matrix (X0^T is its natural layout) or along the natural columns
 // for a wide one (the thread owns the whole 8 x 8 block, so the transpose
-// costs nothing).  Padding elements get u = 0.
-template <typename T>
+// costs nothing).  Padding elements get u = 0.  T is the Newton-Schulz
+// storage type, MT the momentum's (fp32, or bf16 rounded to nearest-even on
+// store; the update and u use the unrounded fp32 value).
+template <typename T, typename MT>
 __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
     __shared__ float red[4];
     const int blk = blockIdx.x;
@@ -67,7 +96,8 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
     T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);  // np rows of ld
     const bool tall = d.transposed != 0;
     const uint8_t* g = a.grads + d.param_off;
-    float* mom = reinterpret_cast<float*>(a.state + d.mom_off);
+    MT* mom = reinterpret_cast<MT*>(a.state + d.mom_off);
+    constexpr int mdt = sizeof(MT) == 2 ? kBF16 : kF32;
     constexpr int SUB = 8, TPR = kK1Tile / SUB;  // threads per tile row of sub-blocks
     const int tx = threadIdx.x % TPR, ty = threadIdx.x / TPR;
     const int r0 = tr * kK1Tile + ty * SUB, c0 = tc * kK1Tile + tx * SUB;
@@ -79,8 +109,9 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
         // all loads of the sub-block first (g and m cannot alias, but the
         // compiler cannot know that), then the arithmetic and the stores
         uint4 graw[SUB];
-        float4 gf[SUB][2], mf[SUB][2];
-        float4* m4 = reinterpret_cast<float4*>(mom + int64_t(r0) * C + c0);
+        float4 gf[SUB][2];
+        typename Mom8<MT>::raw mf[SUB];
+        MT* mrow = mom + int64_t(r0) * C + c0;
         const int ld4 = C / 4;
         if (d.dtype == kBF16) {
             const uint4* g4 = reinterpret_cast<const uint4*>(g) + (int64_t(r0) * C + c0) / 8;
@@ -95,10 +126,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < SUB; ++i) {
-            mf[i][0] = m4[int64_t(i) * ld4];
-            mf[i][1] = m4[int64_t(i) * ld4 + 1];
-        }
+        for (int i = 0; i < SUB; ++i) mf[i] = Mom8<MT>::load(mrow + int64_t(i) * C);
 #pragma unroll
         for (int i = 0; i < SUB; ++i) {
             float gv[8];
@@ -113,16 +141,15 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
                 gv[0] = gf[i][0].x; gv[1] = gf[i][0].y; gv[2] = gf[i][0].z; gv[3] = gf[i][0].w;
                 gv[4] = gf[i][1].x; gv[5] = gf[i][1].y; gv[6] = gf[i][1].z; gv[7] = gf[i][1].w;
             }
-            float mv[8] = {mf[i][0].x, mf[i][0].y, mf[i][0].z, mf[i][0].w,
-                           mf[i][1].x, mf[i][1].y, mf[i][1].z, mf[i][1].w};
+            float mv[8];
+            Mom8<MT>::get(mf[i], mv);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 mv[k] = __builtin_fmaf(a.beta, mv[k], gv[k]);
                 u[i][k] = a.nesterov ? __builtin_fmaf(a.beta, mv[k], gv[k]) : mv[k];
                 ss = __builtin_fmaf(u[i][k], u[i][k], ss);
             }
-            m4[int64_t(i) * ld4] = make_float4(mv[0], mv[1], mv[2], mv[3]);
-            m4[int64_t(i) * ld4 + 1] = make_float4(mv[4], mv[5], mv[6], mv[7]);
+            Vec8<MT>::store(mrow + int64_t(i) * C, mv);
         }
     } else {
         // ragged edge of the matrix (or of the padded tile): element by element
@@ -135,8 +162,8 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
                 if (r < R && c0 + k < C) {
                     const int64_t idx = int64_t(r) * C + c0 + k;
                     const float gk = load_elem(g, d.dtype, idx);
-                    const float mk = __builtin_fmaf(a.beta, mom[idx], gk);
-                    mom[idx] = mk;
+                    const float mk = __builtin_fmaf(a.beta, load_elem(mom, mdt, idx), gk);
+                    store_elem(mom, mdt, idx, mk);
                     u[i][k] = a.nesterov ? __builtin_fmaf(a.beta, mk, gk) : mk;
                 }
                 ss = __builtin_fmaf(u[i][k], u[i][k], ss);
@@ -267,10 +294,18 @@ hipError_t launch_momentum(int ns_precision, const WorkspaceMap& map, const mfsd
     a.partials = reinterpret_cast<float*>(b.ws + map.off_partials);
     a.beta = hp.momentum;
     a.nesterov = hp.nesterov;
-    if (ns_precision == 1)
-        k_momentum<float><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
-    else
-        k_momentum<uint16_t><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
+    const bool mbf = hp.momentum_dtype == kBF16;
+    if (ns_precision == 1) {
+        if (mbf)
+            k_momentum<float, uint16_t><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
+        else
+            k_momentum<float, float><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
+    } else {
+        if (mbf)
+            k_momentum<uint16_t, uint16_t><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
+        else
+            k_momentum<uint16_t, float><<<dim3(map.n_k1_blocks), dim3(256), 0, stream>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_norm_finalize<<<dim3(map.n_mat), dim3(256), 0, stream>>>(

@@ -50,8 +50,11 @@ extern "C" mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64
             return fail(MFSDP_ERR_UNSUPPORTED, "ns_precision must be 0 (bf16) or 1 (fp32)");
         if (!(std::isfinite(pp->flop_rate) && pp->flop_rate > 0 && std::isfinite(pp->byte_rate) && pp->byte_rate > 0))
             return fail(MFSDP_ERR_INVALID_ARGUMENT, "flop_rate and byte_rate must be positive and finite");
+        if (pp->momentum_dtype != MFSDP_F32 && pp->momentum_dtype != MFSDP_BF16)
+            return fail(MFSDP_ERR_UNSUPPORTED, "momentum_dtype must be MFSDP_F32 or MFSDP_BF16");
         const uint64_t cap = pp->mem_cap_bytes;
         const int es_ns = pp->ns_precision == 1 ? 4 : 2;
+        const uint64_t es_mom = pp->momentum_dtype == MFSDP_BF16 ? 2 : 4;
 
         // ---- per-tensor role, cost and memory ----
         std::vector<Item> items(static_cast<size_t>(n));
@@ -83,8 +86,8 @@ extern "C" mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64
                     return fail(MFSDP_ERR_UNSUPPORTED,
                                 "tensor " + std::to_string(i) + ": padded Newton-Schulz buffer of 2 GiB or more");
                 it.cost = double(pp->ns_steps) * (4.0 * m * m * nn + 2.0 * m * m * m) / pp->flop_rate +
-                          double(numel) * double(3 * es + 8 + uint64_t(es_ns)) / pp->byte_rate;
-                it.mem = 2 * region(numel * es) + region(numel * 4) + 2 * region(ld * np * uint64_t(es_ns)) +
+                          double(numel) * double(3 * es + 2 * es_mom + uint64_t(es_ns)) / pp->byte_rate;
+                it.mem = 2 * region(numel * es) + region(numel * es_mom) + 2 * region(ld * np * uint64_t(es_ns)) +
                          2 * region(ld * mp * uint64_t(es_ns));
             } else {
                 it.cost = double(numel) * double(3 * es + 16) / pp->byte_rate;

@@ -43,6 +43,8 @@ mfsdp_status check_hparams(const mfsdp_hparams& hp) {
     if (hp.ns_steps < 0 || hp.ns_steps > 64)
         return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_steps must be in [0, 64]");
     if (hp.ns_eps < 0.f) return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_eps must be >= 0");
+    if (hp.momentum_dtype != MFSDP_F32 && hp.momentum_dtype != MFSDP_BF16)
+        return fail(MFSDP_ERR_UNSUPPORTED, "momentum_dtype must be MFSDP_F32 or MFSDP_BF16");
     if (hp.lr_scale_mode != 0 && hp.lr_scale_mode != 1)
         return fail(MFSDP_ERR_UNSUPPORTED, "lr_scale_mode must be 0 or 1");
     if (hp.ns_precision != 0 && hp.ns_precision != 1)
@@ -173,14 +175,15 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
                             "entries " + std::to_string(i) + " and " + std::to_string(j) + " overlap");
             }
 
-        // ---- state layout: Muon momentum, then AdamW moments (fp32) ----
+        // ---- state layout: Muon momentum (momentum_dtype), then AdamW moments (fp32) ----
+        const uint64_t mom_bytes = hp->momentum_dtype == MFSDP_BF16 ? 2 : 4;
         uint64_t soff = 0;
         for (int64_t i = 0; i < n; ++i) {
             mfsdp_entry_info& inf = plan->info[size_t(i)];
             if (inf.role != MFSDP_ROLE_MUON) continue;
             const uint64_t numel = uint64_t(entries[i].rows) * uint64_t(entries[i].cols);
             inf.state_offset = soff;
-            soff = align_up(soff + numel * 4, kAlign);
+            soff = align_up(soff + numel * mom_bytes, kAlign);
         }
         for (int64_t i = 0; i < n; ++i) {
             mfsdp_entry_info& inf = plan->info[size_t(i)];

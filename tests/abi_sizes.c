@@ -17,7 +17,7 @@ int main(void) {
     OF(mfsdp_hparams, ns_steps); OF(mfsdp_hparams, ns_a); OF(mfsdp_hparams, ns_b); OF(mfsdp_hparams, ns_c);
     OF(mfsdp_hparams, ns_eps); OF(mfsdp_hparams, lr_scale_mode); OF(mfsdp_hparams, ns_precision);
     OF(mfsdp_hparams, adam_lr); OF(mfsdp_hparams, adam_beta1); OF(mfsdp_hparams, adam_beta2); OF(mfsdp_hparams, adam_eps);
-    OF(mfsdp_hparams, adam_weight_decay);
+    OF(mfsdp_hparams, adam_weight_decay); OF(mfsdp_hparams, momentum_dtype);
     SZ(mfsdp_entry_info);
     OF(mfsdp_entry_info, role); OF(mfsdp_entry_info, transposed); OF(mfsdp_entry_info, m); OF(mfsdp_entry_info, n);
     OF(mfsdp_entry_info, state_offset); OF(mfsdp_entry_info, state_offset2); OF(mfsdp_entry_info, ns_out_offset);
@@ -30,7 +30,7 @@ int main(void) {
     OF(mfsdp_tensor, rows); OF(mfsdp_tensor, cols); OF(mfsdp_tensor, dtype); OF(mfsdp_tensor, role);
     SZ(mfsdp_partition_params);
     OF(mfsdp_partition_params, n_owners); OF(mfsdp_partition_params, ns_steps); OF(mfsdp_partition_params, ns_precision);
-    OF(mfsdp_partition_params, reserved); OF(mfsdp_partition_params, mem_cap_bytes);
+    OF(mfsdp_partition_params, momentum_dtype); OF(mfsdp_partition_params, mem_cap_bytes);
     OF(mfsdp_partition_params, flop_rate); OF(mfsdp_partition_params, byte_rate);
     SZ(mfsdp_tensor_place);
     OF(mfsdp_tensor_place, owner); OF(mfsdp_tensor_place, role); OF(mfsdp_tensor_place, offset);

@@ -11,7 +11,9 @@ after step t-1, read back from the device.  Criteria (per matrix / tensor):
 * parameters: the stored W equals RNE(W (1 - lr wd) - lr scale O_gpu) within
   one unit in the last place of the storage type plus one fp32 ulp of W and
   one of lr scale O (the update arithmetic, given the exported O);
-* momentum: relative error <= 1e-6 (one fp32 rounding);
+* momentum: relative error <= 1e-6 (one fp32 rounding); stored in bf16
+  (momentum_dtype): within half a bf16 ulp plus 1e-6 relative of the
+  oracle's value;
 * AdamW tail: relative Frobenius error <= 1e-6 on W, m and v (fp32 tails);
   bf16 tails: within half a bf16 ulp plus 1e-6 relative of the oracle's W.
 """
@@ -113,7 +115,10 @@ class GpuRun:
             v = raw.view(t.bfloat16 if s.dtype == "bf16" else t.float32)
         elif what in ("state", "state2"):
             off = self.info[i].state_offset2 if what == "state2" else self.info[i].state_offset
-            v = self.state[off:off + 4 * s.numel].view(t.float32)
+            if self.momentum_bf16(i) and what == "state":
+                v = self.state[off:off + 2 * s.numel].view(t.bfloat16)
+            else:
+                v = self.state[off:off + 4 * s.numel].view(t.float32)
         else:
             off = self.info[i].ns_out_offset
             v = self.ns_out[off:off + s.numel]
@@ -137,10 +142,14 @@ class GpuRun:
         s = self.wl.specs[i]
         return bytes_to_f64(snap["grads"], self.offs[i], s.rows, s.cols, s.dtype)
 
+    def momentum_bf16(self, i) -> bool:
+        """Entry i is a Muon matrix whose momentum is stored in bf16."""
+        return self.info[i].role == B.ROLE_MUON and int(self.hp.get("momentum_dtype", 0)) == B.BF16
+
     def state_arr(self, snap, i, second=False) -> np.ndarray:
         s = self.wl.specs[i]
         off = self.info[i].state_offset2 if second else self.info[i].state_offset
-        return bytes_to_f64(snap["state"], off, s.rows, s.cols, "f32")
+        return bytes_to_f64(snap["state"], off, s.rows, s.cols, "bf16" if self.momentum_bf16(i) and not second else "f32")
 
     def o_gpu(self, snap, i) -> np.ndarray:
         s = self.wl.specs[i]
@@ -230,10 +239,19 @@ def check_step(run: GpuRun, before, after, step: int, entries=None, sigma=True) 
             full = np.abs(w1 - orc.round_to_dtype(w_orc, s.dtype))
             rep.metrics["w_vs_oracle_max_abs"] = float(full.max())
             m1 = run.state_arr(after, i)
-            mrel = np.max(np.abs(m1 - m_orc)) / max(np.max(np.abs(m_orc)), 1e-30)
-            rep.metrics["mom_rel"] = float(mrel)
-            if not mrel <= 1e-6:
-                rep.failures.append(f"momentum relative error {mrel:.3e} > 1e-6")
+            if run.momentum_bf16(i):
+                # one fp32 FMA, then RNE to bf16: RNE of the oracle's value
+                # except within 1e-6 relative of a bf16 rounding midpoint
+                tol = 0.5 * ulp(m_orc, "bf16") + 1e-6 * np.abs(m_orc)
+                bad = int((np.abs(m1 - m_orc) > tol).sum())
+                rep.metrics["mom_bf16_bad"] = bad
+                if bad:
+                    rep.failures.append(f"bf16 momentum: {bad} elements off RNE(oracle)")
+            else:
+                mrel = np.max(np.abs(m1 - m_orc)) / max(np.max(np.abs(m_orc)), 1e-30)
+                rep.metrics["mom_rel"] = float(mrel)
+                if not mrel <= 1e-6:
+                    rep.failures.append(f"momentum relative error {mrel:.3e} > 1e-6")
         else:
             m0, v0 = run.state_arr(before, i), run.state_arr(before, i, True)
             w_orc, m_orc, v_orc = orc.adamw_step(w0, g, m0, v0, step, hp)

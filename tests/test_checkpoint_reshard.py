@@ -22,11 +22,11 @@ def _model(rng):
 class Owners:
     """Host buffers of every owner of a partition: flat params and state."""
 
-    def __init__(self, shapes, dtypes, n_owners):
-        self.shapes, self.dtypes = shapes, dtypes
-        self.part = B.owner_partition(shapes, dtypes, n_owners)
+    def __init__(self, shapes, dtypes, n_owners, momentum_dtype=B.F32):
+        self.shapes, self.dtypes, self.mdt = shapes, dtypes, momentum_dtype
+        self.part = B.owner_partition(shapes, dtypes, n_owners, momentum_dtype=momentum_dtype)
         self.tables = [self.part.table(o, dtypes, shapes) for o in range(n_owners)]
-        hp = B.make_hparams()
+        hp = B.make_hparams(momentum_dtype=momentum_dtype)
         self.plans = [B.OwnerPlan(t, self.part.owner_param_bytes[o], hp) for o, t in enumerate(self.tables)]
         self.params = [np.zeros(max(1, self.part.owner_param_bytes[o]), np.uint8) for o in range(n_owners)]
         self.state = [np.zeros(max(1, p.state_bytes), np.uint8) for p in self.plans]
@@ -44,7 +44,7 @@ class Owners:
         return t, s1, s2
 
     def gather(self):
-        full = empty_checkpoint(self.shapes, self.dtypes, self.part.role)
+        full = empty_checkpoint(self.shapes, self.dtypes, self.part.role, self.mdt)
         for o, plan in enumerate(self.plans):
             t, s1, s2 = self._bufs(o, full)
             plan.gather(self.params[o].ctypes.data, self.params[o].size, self.state[o].ctypes.data,
@@ -58,23 +58,26 @@ class Owners:
                          self.state[o].size)
 
 
-def empty_checkpoint(shapes, dtypes, roles):
+def empty_checkpoint(shapes, dtypes, roles, momentum_dtype=B.F32):
     param = [np.zeros(r * c * (2 if dt == B.BF16 else 4), np.uint8) for (r, c), dt in zip(shapes, dtypes)]
-    s1 = [np.zeros(r * c, np.float32) if r * c else None for (r, c) in shapes]
+    # Muon momentum in the plan's momentum type (bf16 as raw 16-bit words), AdamW moments fp32
+    s1 = [(np.zeros(r * c, np.uint16) if ro == B.ROLE_MUON and momentum_dtype == B.BF16 else np.zeros(r * c, np.float32))
+          if r * c else None for (r, c), ro in zip(shapes, roles)]
     s2 = [np.zeros(r * c, np.float32) if r * c and ro == B.ROLE_ADAMW else None
           for (r, c), ro in zip(shapes, roles)]
     return {"param": param, "s1": s1, "s2": s2}
 
 
-def random_checkpoint(rng, shapes, dtypes, roles):
-    full = empty_checkpoint(shapes, dtypes, roles)
+def random_checkpoint(rng, shapes, dtypes, roles, momentum_dtype=B.F32):
+    full = empty_checkpoint(shapes, dtypes, roles, momentum_dtype)
     for i in range(len(shapes)):
         full["param"][i][:] = rng.integers(0, 256, full["param"][i].size, dtype=np.uint8)
         for k in ("s1", "s2"):
             if full[k][i] is not None:
                 # arbitrary bit patterns, NaN payloads and signed zeros included
-                full[k][i][:] = rng.integers(0, 2 ** 32, full[k][i].size, dtype=np.uint64).astype(np.uint32).view(
-                    np.float32)
+                bits = rng.integers(0, 2 ** 32, full[k][i].size, dtype=np.uint64)
+                full[k][i][:] = (bits.astype(np.uint16) if full[k][i].dtype == np.uint16
+                                 else bits.astype(np.uint32).view(np.float32))
     return full
 
 
@@ -87,15 +90,15 @@ def _same(a, b):
                 assert x.view(np.uint8).tobytes() == y.view(np.uint8).tobytes()
 
 
-@pytest.mark.parametrize("old,new", [(4, 3), (1, 5), (6, 2)])
-def test_reshard_round_trip_bit_exact(old, new):
+@pytest.mark.parametrize("old,new,mdt", [(4, 3, B.F32), (1, 5, B.F32), (6, 2, B.F32), (3, 5, B.BF16)])
+def test_reshard_round_trip_bit_exact(old, new, mdt):
     rng = np.random.default_rng(old * 10 + new)
     shapes, dtypes = _model(rng)
-    a = Owners(shapes, dtypes, old)
-    b = Owners(shapes, dtypes, new)
-    c = Owners(shapes, dtypes, old)
+    a = Owners(shapes, dtypes, old, mdt)
+    b = Owners(shapes, dtypes, new, mdt)
+    c = Owners(shapes, dtypes, old, mdt)
     try:
-        ckpt = random_checkpoint(rng, shapes, dtypes, a.part.role)
+        ckpt = random_checkpoint(rng, shapes, dtypes, a.part.role, mdt)
         a.scatter(ckpt)
         full1 = a.gather()
         _same(full1, ckpt)

@@ -2,7 +2,8 @@
 not reach: Newton-Schulz step counts 0, 1 and 2 (no iteration: the update
 straight from the normalised input; the first iteration also being the
 last), the alternative learning-rate shape scale, plain (non-Nesterov)
-momentum, explicit role overrides, the 256-tile kernels on ragged shapes
+momentum, momentum stored in bf16, explicit role overrides, the 256-tile
+kernels on ragged shapes
 (also with other iteration coefficients), and bitwise run-to-run
 determinism."""
 
@@ -58,6 +59,18 @@ def test_role_overrides():
     finally:
         run.free()
     _steps(wl, 2, label="roles")
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_bf16_momentum(precision):
+    """Momentum stored in bf16 (momentum_dtype): three steps, so that the
+    second and third read back the rounded state; the ragged table takes the
+    element-wise edge path and the vector path of the momentum kernel."""
+    _steps(W.small_ragged(precision=precision), 3, {"momentum_dtype": 1}, label=f"mom-bf16-p{precision}")
+
+
+def test_bf16_momentum_gpt2():
+    _steps(W.config(1), 2, {"momentum_dtype": 1}, label="mom-bf16-gpt2")
 
 
 @pytest.mark.parametrize("precision", [0, 1])

@@ -18,7 +18,7 @@ def _region(x):
     return (x + 255) // 256 * 256
 
 
-def _model(rows, cols, dtype, role=B.ROLE_AUTO, ns_steps=5, es_ns=2):
+def _model(rows, cols, dtype, role=B.ROLE_AUTO, ns_steps=5, es_ns=2, em=4):
     """Cost (s) and memory (bytes) of one tensor by the model stated in mfsdp.h."""
     es = 2 if dtype == B.BF16 else 4
     numel = rows * cols
@@ -28,8 +28,8 @@ def _model(rows, cols, dtype, role=B.ROLE_AUTO, ns_steps=5, es_ns=2):
     if muon:
         m, n = min(rows, cols), max(rows, cols)
         mp, np_ = -(-m // 256) * 256, -(-n // 256) * 256
-        cost = ns_steps * (4 * m * m * n + 2 * m ** 3) / FLOP + numel * (3 * es + 8 + es_ns) / BYTE
-        mem = 2 * _region(numel * es) + _region(numel * 4) + 2 * _region(mp * np_ * es_ns) + 2 * _region(mp * mp * es_ns)
+        cost = ns_steps * (4 * m * m * n + 2 * m ** 3) / FLOP + numel * (3 * es + 2 * em + es_ns) / BYTE
+        mem = 2 * _region(numel * es) + _region(numel * em) + 2 * _region(mp * np_ * es_ns) + 2 * _region(mp * mp * es_ns)
     else:
         cost = numel * (3 * es + 16) / BYTE
         mem = 2 * _region(numel * es) + 2 * _region(numel * 4)
@@ -62,6 +62,11 @@ def test_cost_and_memory_model():
     p = B.owner_partition([(512, 1024)], [B.BF16], 1, ns_steps=3, ns_precision=1)
     cost, mem, _ = _model(512, 1024, B.BF16, ns_steps=3, es_ns=4)
     assert math.isclose(p.cost[0], cost, rel_tol=1e-12) and p.mem_bytes[0] == mem
+    # bf16 momentum: 2 B per Muon element of state, 4 B less traffic
+    p = B.owner_partition(shapes, dtypes, 3, flop_rate=FLOP, byte_rate=BYTE, momentum_dtype=B.BF16)
+    for i, (sh, dt) in enumerate(zip(shapes, dtypes)):
+        cost, mem, _ = _model(*sh, dt, em=2)
+        assert math.isclose(p.cost[i], cost, rel_tol=1e-12) and p.mem_bytes[i] == mem, i
 
 
 @pytest.mark.parametrize("n_owners", [2, 3])
@@ -116,8 +121,9 @@ def _llama_layers(layers, d, kv, ffn):
     return shapes, dtypes
 
 
-@pytest.mark.parametrize("model,n_owners", [("llama3-8b", 8), ("llama3-70b", 8), ("llama3-8b", 6)])
-def test_whole_model_balance_and_tables(model, n_owners):
+@pytest.mark.parametrize("model,n_owners,mdt", [("llama3-8b", 8, 0), ("llama3-70b", 8, 0), ("llama3-8b", 6, 0),
+                                                ("llama3-8b", 8, 1)])
+def test_whole_model_balance_and_tables(model, n_owners, mdt):
     """Every Muon matrix of a Llama-3 model over n_owners: owner costs within
     1% of each other's mean, and each owner's table (input order, returned
     offsets) is a plan mfsdp_plan_create accepts whose state, workspace and
@@ -127,10 +133,10 @@ def test_whole_model_balance_and_tables(model, n_owners):
         shapes, dtypes = _llama_layers(32, 4096, 1024, 14336)
     else:
         shapes, dtypes = _llama_layers(80, 8192, 1024, 28672)
-    p = B.owner_partition(shapes, dtypes, n_owners)
+    p = B.owner_partition(shapes, dtypes, n_owners, momentum_dtype=mdt)
     mean = sum(p.owner_cost) / n_owners
     assert max(p.owner_cost) <= 1.01 * mean, (max(p.owner_cost), mean)
-    hp = B.make_hparams()
+    hp = B.make_hparams(momentum_dtype=mdt)
     for o in range(n_owners):
         table = p.table(o, dtypes, shapes)
         offs = [e.offset for e in table]
@@ -168,6 +174,7 @@ def test_argument_errors():
     assert status(flop_rate=0.0) == 1
     assert status(byte_rate=float("inf")) == 1
     assert status(ns_steps=-1) == 1
+    assert status(momentum_dtype=2) == 4
     assert status(ns_precision=2) == 4
     assert status(dtypes=[7]) == 4
     assert status(roles=[9]) == 4

@@ -90,6 +90,7 @@ def test_validation_errors():
     assert _status([E(0, 4, 4)], ns_steps=65) == 1
     assert _status([E(0, 4, 4)], ns_precision=2) == 4
     assert _status([E(0, 4, 4)], lr_scale_mode=3) == 4
+    assert _status([E(0, 4, 4)], momentum_dtype=2) == 4
     assert _status([E(0, 4, 4)], lr=float("nan")) == 1
     assert _status([E(0, 4, 4)], adam_beta2=1.0) == 1
     assert _status([]) == 0                                          # empty table is legal
@@ -120,17 +121,27 @@ def test_routing_orientation_and_scale():
     assert _plan([E(0, 4, 4)], ns_steps=0).num_events() == 3
 
 
-def test_state_and_ns_out_layout():
+@pytest.mark.parametrize("mdt", [0, 1])
+def test_state_and_ns_out_layout(mdt):
     wl = W.small_ragged()
     offs, pbytes = wl.layout()
     dt = {"bf16": B.BF16, "f32": B.F32}
     p = B.OwnerPlan([B.TableEntry(o, s.rows, s.cols, dt[s.dtype]) for o, s in zip(offs, wl.specs)], pbytes,
-                    B.make_hparams())
+                    B.make_hparams(momentum_dtype=mdt))
+    em = 2 if mdt == 1 else 4
     regions, ns = [], []
+    want_state = 0
     for i, s in enumerate(wl.specs):
         inf = p.entry_info(i)
         if inf.role == 1:
-            regions.append((inf.state_offset, s.numel * 4))
+            want_state += -(-s.numel * em // 256) * 256
+        elif inf.role == 2:
+            want_state += 2 * (-(-s.numel * 4 // 256) * 256)
+    assert p.state_bytes == want_state
+    for i, s in enumerate(wl.specs):
+        inf = p.entry_info(i)
+        if inf.role == 1:
+            regions.append((inf.state_offset, s.numel * em))
             ns.append((inf.ns_out_offset, s.numel))
         elif inf.role == 2:
             regions += [(inf.state_offset, s.numel * 4), (inf.state_offset2, s.numel * 4)]
