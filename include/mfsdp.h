@@ -146,12 +146,20 @@ typedef struct mfsdp_step_args {
  * buffer, used for bounds checks.  hp: copied into the plan.
  * Errors: INVALID_ARGUMENT (null pointer, n < 0, negative dim, entry past
  * param_bytes, bad hyper-parameter), OVERLAP, MISALIGNED, UNSUPPORTED (dtype,
- * role, ns_precision, a dimension above 2^22).  *out is set only on success. */
+ * role, ns_precision, momentum_dtype, a dimension above 2^22, a Muon matrix
+ * whose padded Newton-Schulz buffer reaches 2 GiB).  *out is set only on
+ * success.
+ * The environment variable MFSDP_TILE, read here, overrides the output tile
+ * edge of the Newton-Schulz contractions (for tests and tuning): "E" for
+ * every phase or "G,P,U" for the Gram, polynomial and update phases, each
+ * 128 or 256; other values are ignored.  By default a phase uses 256 when it
+ * has at least 512 tiles of that edge, else 128. */
 mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n, uint64_t param_bytes,
                                const mfsdp_hparams* hp, mfsdp_plan_t* out);
 
-/* Bytes of optimizer state the plan lays out (fp32 momentum for Muon entries,
- * then fp32 first and second moments for AdamW entries). */
+/* Bytes of optimizer state the plan lays out (momentum for Muon entries, fp32
+ * or bf16 by hp->momentum_dtype, then fp32 first and second moments for AdamW
+ * entries), each region 256-byte aligned. */
 mfsdp_status mfsdp_plan_state_bytes(mfsdp_plan_t plan, uint64_t* bytes);
 
 /* Bytes of device workspace one step needs (descriptors, norm partials,

@@ -66,7 +66,7 @@ def oracle_hparams(hp: Dict[str, float]) -> orc.Hparams:
         adam_eps=f(hp["adam_eps"]), adam_weight_decay=f(hp["adam_weight_decay"]))
 
 
-class GpuRun:
+class DeviceRun:
     """One workload's plan and device buffers."""
 
     def __init__(self, wl: W.Workload, hp_overrides=None, device="cuda"):
@@ -188,7 +188,7 @@ def sigma_check(o_gpu: np.ndarray, o_orc: np.ndarray) -> float:
     return float(np.max(np.abs(spec(o_gpu) - spec(o_orc))))
 
 
-def check_step(run: GpuRun, before, after, step: int, entries=None, sigma=True) -> List[EntryReport]:
+def check_step(run: DeviceRun, before, after, step: int, entries=None, sigma=True) -> List[EntryReport]:
     """Compare one GPU step (host copies before/after) with the oracle."""
     hp = oracle_hparams(run.hp)
     prec = int(run.hp["ns_precision"])

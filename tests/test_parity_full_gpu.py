@@ -15,7 +15,7 @@ import pytest
 
 from matrix_optimizer_owner_amd import workloads as W
 from oracle import muon_oracle as orc
-from tests.harness import GpuRun, oracle_hparams, say, sigma_check, ulp
+from tests.harness import DeviceRun, oracle_hparams, say, sigma_check, ulp
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -75,7 +75,7 @@ def check_elementwise(run, snap, i, hp, rng, samples=4096):
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_two_iterations_sketch_full_size(cfg):
     wl = W.config(cfg)
-    run = GpuRun(wl, {"ns_steps": 2})
+    run = DeviceRun(wl, {"ns_steps": 2})
     hp = oracle_hparams(run.hp)
     idxs = pick(wl, 4)
     say(f"[sketch cfg{cfg}] {wl.name}: checking {[(wl.specs[i].rows, wl.specs[i].cols) for i in idxs]}")
@@ -101,7 +101,7 @@ def test_two_iterations_sketch_full_size(cfg):
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_five_iterations_full_size(cfg):
     wl = W.config(cfg)
-    run = GpuRun(wl)
+    run = DeviceRun(wl)
     hp = oracle_hparams(run.hp)
     cheap = cheapest(wl, 4, 1024 * 1024 * 8192)
     idxs = sorted(set(pick(wl, 4) + cheap))
@@ -146,7 +146,7 @@ def test_ten_consecutive_steps_llama3_8b_share():
     """The 8B owner share runs 10 consecutive steps with fresh gradients;
     each step is checked teacher-forced on its cheapest matrices."""
     wl = W.config(2)
-    run = GpuRun(wl)
+    run = DeviceRun(wl)
     hp = oracle_hparams(run.hp)
     idxs = cheapest(wl, 1, 1024 * 1024 * 4096)  # the 1024x4096 k projection
     rng = np.random.default_rng(7)
@@ -176,7 +176,7 @@ def test_free_running_drift_llama3_8b_share():
     Frobenius distance of W stays below 5e-3 and of the momentum (which does
     not depend on O) below 1e-5."""
     wl = W.config(2)
-    run = GpuRun(wl)
+    run = DeviceRun(wl)
     hp = oracle_hparams(run.hp)
     idxs = [i for i, s in enumerate(wl.specs) if (s.rows, s.cols) == (1024, 4096)][:2]
     assert len(idxs) == 2
