@@ -12,10 +12,11 @@ after step t-1, read back from the device.  Criteria (per matrix / tensor):
   one unit in the last place of the storage type plus one fp32 ulp of W and
   one of lr scale O (the update arithmetic, given the exported O);
 * momentum: relative error <= 1e-6 (one fp32 rounding); stored in bf16
-  (momentum_dtype): within half a bf16 ulp plus 1e-6 relative of the
-  oracle's value;
+  (momentum_dtype): within half a bf16 ulp of the oracle's value plus 1e-6
+  of the larger operand (beta m or g);
 * AdamW tail: relative Frobenius error <= 1e-6 on W, m and v (fp32 tails);
-  bf16 tails: within half a bf16 ulp plus 1e-6 relative of the oracle's W.
+  bf16 tails: within half a bf16 ulp of the oracle's W plus 1e-6 of the
+  larger operand of the update (the fp32 error before the rounding).
 """
 
 from __future__ import annotations
@@ -241,8 +242,11 @@ def check_step(run: DeviceRun, before, after, step: int, entries=None, sigma=Tru
             m1 = run.state_arr(after, i)
             if run.momentum_bf16(i):
                 # one fp32 FMA, then RNE to bf16: RNE of the oracle's value
-                # except within 1e-6 relative of a bf16 rounding midpoint
-                tol = 0.5 * ulp(m_orc, "bf16") + 1e-6 * np.abs(m_orc)
+                # except within 1e-6 of a bf16 rounding midpoint, relative to
+                # the larger operand (beta m or g: the fp32 error scales with
+                # them, not with a result that may cancel)
+                scale = np.maximum(np.abs(hp.momentum * m0), np.abs(g))
+                tol = 0.5 * ulp(m_orc, "bf16") + 1e-6 * np.maximum(scale, np.abs(m_orc))
                 bad = int((np.abs(m1 - m_orc) > tol).sum())
                 rep.metrics["mom_bf16_bad"] = bad
                 if bad:
@@ -267,7 +271,15 @@ def check_step(run: DeviceRun, before, after, step: int, entries=None, sigma=Tru
                 if not d <= 1e-6:
                     rep.failures.append(f"AdamW W relative error {d:.3e} > 1e-6")
             else:
-                tol = 0.5 * ulp(w_orc, "bf16") + 1e-6 * np.abs(w_orc)
+                # RNE of the oracle's W except within 1e-6 of a bf16 rounding
+                # midpoint, relative to the larger operand of the update (W or
+                # lr m_hat / (sqrt(v_hat) + eps)): the kernel's fp32 error
+                # scales with them, and the two may cancel
+                m_hat = m_orc / (1.0 - hp.adam_beta1 ** step)
+                v_hat = v_orc / (1.0 - hp.adam_beta2 ** step)
+                step_term = hp.adam_lr * np.abs(m_hat) / (np.sqrt(v_hat) + hp.adam_eps)
+                scale = np.maximum(np.maximum(np.abs(w0), step_term), np.abs(w_orc))
+                tol = 0.5 * ulp(w_orc, "bf16") + 1e-6 * scale
                 bad = np.abs(w1 - w_orc) > tol
                 rep.metrics["adam_w_bf16_bad"] = int(bad.sum())
                 if bad.any():

@@ -51,14 +51,27 @@ def test_role_overrides():
         W.TensorSpec("forced_muon", 130, 70, role="muon", grad_std=1e-2),
         W.TensorSpec("auto_matrix", 64, 300, grad_std=1e-3),
         W.TensorSpec("auto_vector", 1, 500, "f32", grad_std=1e-3),
+        W.TensorSpec("forced_muon_row", 1, 300, role="muon", grad_std=1e-3),
+        W.TensorSpec("forced_muon_col", 300, 1, "f32", role="muon", grad_std=1e-3),
     ]
     wl = W.Workload("role-overrides", sp, seed=11, hparams=dict(W.MUON_DEFAULTS, ns_precision=0))
     run = DeviceRun(wl)
     try:
-        assert [run.info[i].role for i in range(4)] == [B.ROLE_ADAMW, B.ROLE_MUON, B.ROLE_MUON, B.ROLE_ADAMW]
+        assert [run.info[i].role for i in range(6)] == [B.ROLE_ADAMW, B.ROLE_MUON, B.ROLE_MUON, B.ROLE_ADAMW,
+                                                        B.ROLE_MUON, B.ROLE_MUON]
     finally:
         run.free()
     _steps(wl, 2, label="roles")
+
+
+def test_tail_only_table():
+    """No Muon matrix at all: only the AdamW kernel runs (fp32 and bf16
+    vectors, a scalar, a forced-AdamW matrix), over three steps of bias
+    correction."""
+    sp = [W.TensorSpec("v32", 1, 4099, "f32", grad_std=1e-3), W.TensorSpec("v16", 1, 2048 * 3 + 5, "bf16", grad_std=1e-2),
+          W.TensorSpec("s", 1, 1, "f32", "ones", grad_std=1.0),
+          W.TensorSpec("m", 64, 96, "f32", role="adamw", grad_std=1e-3)]
+    _steps(W.Workload("tail-only", sp, seed=12, hparams=dict(W.MUON_DEFAULTS, ns_precision=0)), 3, label="tail-only")
 
 
 @pytest.mark.parametrize("precision", [0, 1])
