@@ -27,6 +27,8 @@ constexpr int kPad = 256;          // padding granule of m and n in the workspac
 constexpr int kTileSmall = 128;    // output tile edges of the contraction kernels
 constexpr int kTileLarge = 256;
 constexpr int kLargeTileMin = 512; // a phase uses 256-tiles when it has at least this many
+constexpr int kCus = 256;          // compute units of the part (one 256-tile block each)
+constexpr int kSplitTailMax = 64;  // a last update round of at most this many 256-tiles runs as 128-tiles
 constexpr int kK1Tile = 128;       // tile edge of the momentum kernel
 // Row pitch pad (elements) of the Newton-Schulz buffers beyond mp.  Pads of
 // 64 and 128 elements (against the power-of-two pitch of most shapes)
@@ -81,11 +83,12 @@ static_assert(sizeof(TailDesc) == 40, "TailDesc layout");
 // workspace regions, plus element counts; filled by the planner.
 struct WorkspaceMap {
     uint64_t desc_bytes;
-    uint64_t off_mat, off_k1_begin, off_gram, off_poly, off_upd, off_tail, off_tail_begin;
+    uint64_t off_mat, off_k1_begin, off_gram, off_poly, off_upd, off_upd_tail, off_tail, off_tail_begin;
     uint64_t off_s, off_partials;
     uint64_t total_bytes;
     int32_t n_mat, n_tail;
     int32_t n_gram, n_poly, n_upd;
+    int32_t n_upd_tail;                      // 128-tiles run after the 256-tile update list (see the planner)
     int32_t n_k1_blocks, n_tail_chunks;
     int32_t tile_gram, tile_poly, tile_upd;  // tile edge of each contraction phase
 };

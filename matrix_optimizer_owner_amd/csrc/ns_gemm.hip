@@ -1128,11 +1128,20 @@ hipError_t launch_phase(const WorkspaceMap& map, const mfsdp_hparams& hp, int it
         a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_poly);
         launch_tiles<T, kPoly>(a, map.n_poly, map.tile_poly, stream);
     } else {
+        // the planner's 256-tile list, then its 128-tile remainder (if any)
+        const bool fin = iter == hp.ns_steps;
         a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_upd);
-        if (iter == hp.ns_steps)
+        if (fin)
             launch_tiles<T, kFinal>(a, map.n_upd, map.tile_upd, stream);
         else
             launch_tiles<T, kUpdate>(a, map.n_upd, map.tile_upd, stream);
+        if (map.n_upd_tail > 0) {
+            a.tiles = reinterpret_cast<const Tile*>(b.ws + map.off_upd_tail);
+            if (fin)
+                launch_tiles<T, kFinal>(a, map.n_upd_tail, kTileSmall, stream);
+            else
+                launch_tiles<T, kUpdate>(a, map.n_upd_tail, kTileSmall, stream);
+        }
     }
     return hipGetLastError();
 }

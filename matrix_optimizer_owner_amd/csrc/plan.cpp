@@ -298,6 +298,22 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         gram = xcd_order(gram);
         poly = xcd_order(poly);
         upd = xcd_order(upd);
+        // Wave quantisation of the update: when a 256-tile list would leave a
+        // last round of at most kSplitTailMax tiles (one block per CU, so most
+        // CUs idle for a whole tile time), those tiles run instead as four
+        // 128-tiles each in a second launch (two blocks per CU), which ends in
+        // about half a 256-tile time.  Not applied when the tile edge is forced.
+        std::vector<Tile> upd_tail;
+        if (tu == kTileLarge && !forced[2]) {
+            const size_t r = upd.size() % size_t(kCus);
+            if (r > 0 && r <= size_t(kSplitTailMax) && upd.size() > r) {
+                for (size_t k = upd.size() - r; k < upd.size(); ++k)
+                    for (int i = 0; i < 2; ++i)
+                        for (int j = 0; j < 2; ++j)
+                            upd_tail.push_back(Tile{upd[k].mat, uint16_t(2 * upd[k].ti + i), uint16_t(2 * upd[k].tj + j)});
+                upd.resize(upd.size() - r);
+            }
+        }
 
         std::vector<int32_t> k1_begin(1, 0);
         for (const MatDesc& d : mats) {
@@ -328,6 +344,7 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         w.off_gram = section(gram.size() * sizeof(Tile));
         w.off_poly = section(poly.size() * sizeof(Tile));
         w.off_upd = section(upd.size() * sizeof(Tile));
+        w.off_upd_tail = section(upd_tail.size() * sizeof(Tile));
         w.off_tail = section(tails.size() * sizeof(TailDesc));
         w.off_tail_begin = section(tail_begin.size() * sizeof(int32_t));
         w.desc_bytes = off;
@@ -348,6 +365,7 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         w.n_gram = int32_t(gram.size());
         w.n_poly = int32_t(poly.size());
         w.n_upd = int32_t(upd.size());
+        w.n_upd_tail = int32_t(upd_tail.size());
         w.n_k1_blocks = k1_begin.back();
         w.n_tail_chunks = tail_begin.back();
         w.tile_gram = tg;
@@ -363,6 +381,7 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         put(w.off_gram, gram.data(), gram.size() * sizeof(Tile));
         put(w.off_poly, poly.data(), poly.size() * sizeof(Tile));
         put(w.off_upd, upd.data(), upd.size() * sizeof(Tile));
+        put(w.off_upd_tail, upd_tail.data(), upd_tail.size() * sizeof(Tile));
         put(w.off_tail, tails.data(), tails.size() * sizeof(TailDesc));
         put(w.off_tail_begin, tail_begin.data(), tail_begin.size() * sizeof(int32_t));
     } catch (const std::bad_alloc&) {

@@ -140,7 +140,31 @@ int main() {
     };
     check_tiles(w.off_gram, w.n_gram, w.tile_gram, true, false, "gram");
     check_tiles(w.off_poly, w.n_poly, w.tile_poly, true, false, "poly");
-    check_tiles(w.off_upd, w.n_upd, w.tile_upd, false, true, "update");
+    if (w.n_upd_tail == 0) {
+        check_tiles(w.off_upd, w.n_upd, w.tile_upd, false, true, "update");
+    } else {
+        // a 256-tile list plus a 128-tile remainder: together every 128-cell once
+        CHECK(w.tile_upd == 256 && w.n_upd % 256 == 0 && w.n_upd_tail % 4 == 0 && w.n_upd_tail <= 4 * 64,
+              "update split shape %d + %d", w.n_upd, w.n_upd_tail);
+        std::set<std::tuple<uint32_t, int, int>> cells;
+        size_t expect = 0, got = 0;
+        for (int k = 0; k < w.n_mat; ++k) expect += size_t(mats[k].mp / 128) * (mats[k].np / 128);
+        const Tile* t = reinterpret_cast<const Tile*>(blob + w.off_upd);
+        for (int k = 0; k < w.n_upd; ++k)
+            for (int i = 0; i < 2; ++i)
+                for (int j = 0; j < 2; ++j) {
+                    CHECK(t[k].mat < uint32_t(w.n_mat) && t[k].ti < mats[t[k].mat].mp / 256 && t[k].tj < mats[t[k].mat].np / 256,
+                          "update tile %d out of range", k);
+                    got += cells.insert({t[k].mat, 2 * t[k].ti + i, 2 * t[k].tj + j}).second;
+                }
+        const Tile* u = reinterpret_cast<const Tile*>(blob + w.off_upd_tail);
+        for (int k = 0; k < w.n_upd_tail; ++k) {
+            CHECK(u[k].mat < uint32_t(w.n_mat) && u[k].ti < mats[u[k].mat].mp / 128 && u[k].tj < mats[u[k].mat].np / 128,
+                  "update tail tile %d out of range", k);
+            got += cells.insert({u[k].mat, u[k].ti, u[k].tj}).second;
+        }
+        CHECK(got == size_t(w.n_upd) * 4 + size_t(w.n_upd_tail) && got == expect, "update cells %zu of %zu", got, expect);
+    }
     CHECK(w.tile_gram == 128 || w.tile_gram == 256, "gram tile edge");
     CHECK(w.tile_upd == 128 || w.tile_upd == 256, "update tile edge");
 
@@ -172,8 +196,8 @@ int main() {
         if (k) CHECK(sregs[k - 1].first + sregs[k - 1].second <= sregs[k].first, "state regions overlap");
     }
     if (!fail_count)
-        std::printf("OK mats=%d tails=%d gram=%d poly=%d upd=%d tiles=%d/%d/%d ws=%llu state=%llu\n", w.n_mat,
-                    w.n_tail, w.n_gram, w.n_poly, w.n_upd, w.tile_gram, w.tile_poly, w.tile_upd,
+        std::printf("OK mats=%d tails=%d gram=%d poly=%d upd=%d+%d tiles=%d/%d/%d ws=%llu state=%llu\n", w.n_mat,
+                    w.n_tail, w.n_gram, w.n_poly, w.n_upd, w.n_upd_tail, w.tile_gram, w.tile_poly, w.tile_upd,
                     (unsigned long long)w.total_bytes, (unsigned long long)plan->state_bytes);
     mfsdp_plan_destroy(plan);
     return fail_count ? 1 : 0;

@@ -196,6 +196,20 @@ def test_plan_descriptor_invariants(plan_checker, name):
     assert res.stdout.startswith("OK"), res.stdout
 
 
+def test_update_wave_tail_split(plan_checker):
+    """GPT-2: 1296 update tiles of 256 are five full rounds of 256 CUs plus
+    16; those 16 run as 64 tiles of 128 in a second launch.  The Llama-3-8B
+    share (13312 = 52 x 256) has no remainder; a forced tile edge disables
+    the split."""
+    out = subprocess.run([plan_checker], input=_table_text(W.config(1)), capture_output=True, text=True).stdout
+    assert "upd=1280+64 " in out, out
+    out = subprocess.run([plan_checker], input=_table_text(W.config(2)), capture_output=True, text=True).stdout
+    assert "upd=13312+0 " in out, out
+    out = subprocess.run([plan_checker], input=_table_text(W.config(1)), capture_output=True, text=True,
+                         env=dict(os.environ, MFSDP_TILE="256")).stdout
+    assert "upd=1296+0 " in out, out
+
+
 def test_tile_override_keeps_invariants(plan_checker):
     wl = W.config(1)
     for t in ("128", "256", "256,128,256"):
