@@ -256,7 +256,47 @@ struct AdamArgs {
     float lr, lrwd, eps;
 };
 
+// Eight consecutive parameter / gradient elements (fp32, or bf16 rounded to
+// nearest-even on store) as 16-byte vectors.
+__device__ __forceinline__ void load8(const uint8_t* base, int dtype, int64_t i, float (&v)[8]) {
+    if (dtype == kBF16) {
+        const uint4 r = *reinterpret_cast<const uint4*>(base + 2 * i);
+        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(u[k] << 16);
+            v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(base + 4 * i);
+        const float4 x = p[0], y = p[1];
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    }
+}
+__device__ __forceinline__ void store8(uint8_t* base, int dtype, int64_t i, const float (&v)[8]) {
+    if (dtype == kBF16)
+        Vec8<uint16_t>::store(reinterpret_cast<uint16_t*>(base) + i, v);
+    else
+        Vec8<float>::store(reinterpret_cast<float*>(base) + i, v);
+}
+
+__device__ __forceinline__ void adamw_elem(const AdamArgs& a, float gv, float& wv, float& m, float& v) {
+    m = a.b1 * m + a.omb1 * gv;
+    v = a.b2 * v + a.omb2 * (gv * gv);
+    const float mhat = m * a.inv_bc1;
+    const float vhat = v * a.inv_bc2;
+    const float upd = mhat / (sqrtf(vhat) + a.eps);
+    wv = __builtin_fmaf(-a.lr, upd, __builtin_fmaf(-a.lrwd, wv, wv));
+}
+
+// One block per kTailChunk (= 256 threads x 8) elements of one tail tensor;
+// each thread owns 8 consecutive elements, read and written as 16-byte
+// vectors (tensor offsets are 16-byte aligned, the moments 256-byte
+// aligned, chunk starts a multiple of 2048 elements), the tensor's last
+// partial group element by element.
 __global__ __launch_bounds__(256) void k_adamw(AdamArgs a) {
+    static_assert(kTailChunk == 256 * 8, "eight elements per thread");
     const int chunk = blockIdx.x;
     const int ti = upper_index(a.tail_begin, a.n_tail, chunk);
     const TailDesc t = a.tails[ti];
@@ -266,17 +306,26 @@ __global__ __launch_bounds__(256) void k_adamw(AdamArgs a) {
     const uint8_t* g = a.grads + t.param_off;
     float* m1 = reinterpret_cast<float*>(a.state + t.m1_off);
     float* m2 = reinterpret_cast<float*>(a.state + t.m2_off);
-    for (int64_t i = begin + threadIdx.x; i < end; i += 256) {
-        const float gv = load_elem(g, t.dtype, i);
-        const float wv = load_elem(w, t.dtype, i);
-        const float m = a.b1 * m1[i] + a.omb1 * gv;
-        const float v = a.b2 * m2[i] + a.omb2 * (gv * gv);
-        m1[i] = m;
-        m2[i] = v;
-        const float mhat = m * a.inv_bc1;
-        const float vhat = v * a.inv_bc2;
-        const float upd = mhat / (sqrtf(vhat) + a.eps);
-        store_elem(w, t.dtype, i, __builtin_fmaf(-a.lr, upd, __builtin_fmaf(-a.lrwd, wv, wv)));
+    const int64_t i0 = begin + int64_t(threadIdx.x) * 8;
+    if (i0 + 8 <= end) {
+        float gv[8], wv[8], mv[8], vv[8];
+        load8(g, t.dtype, i0, gv);
+        load8(w, t.dtype, i0, wv);
+        load8(reinterpret_cast<const uint8_t*>(m1), kF32, i0, mv);
+        load8(reinterpret_cast<const uint8_t*>(m2), kF32, i0, vv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) adamw_elem(a, gv[k], wv[k], mv[k], vv[k]);
+        store8(reinterpret_cast<uint8_t*>(m1), kF32, i0, mv);
+        store8(reinterpret_cast<uint8_t*>(m2), kF32, i0, vv);
+        store8(w, t.dtype, i0, wv);
+    } else {
+        for (int64_t i = i0; i < end; ++i) {
+            float wv = load_elem(w, t.dtype, i), m = m1[i], v = m2[i];
+            adamw_elem(a, load_elem(g, t.dtype, i), wv, m, v);
+            m1[i] = m;
+            m2[i] = v;
+            store_elem(w, t.dtype, i, wv);
+        }
     }
 }
 
