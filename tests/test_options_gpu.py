@@ -64,6 +64,16 @@ def test_role_overrides():
     _steps(wl, 2, label="roles")
 
 
+def test_zero_gradient_matrices():
+    """Degenerate Muon inputs: an all-zero gradient with zero momentum gives
+    u = 0, so O = 0 and the parameter update is the pure decay W (1 - lr wd)
+    (bf16 parameters, a ragged shape, an fp32 parameter), next to an
+    ordinary matrix; two steps."""
+    sp = [W.TensorSpec("zero_bf16", 512, 768, grad_std=0.0), W.TensorSpec("zero_small", 70, 130, grad_std=0.0),
+          W.TensorSpec("zero_f32", 96, 64, "f32", grad_std=0.0), W.TensorSpec("normal", 300, 200, grad_std=1e-3)]
+    _steps(W.Workload("zero-grads", sp, seed=13, hparams=dict(W.MUON_DEFAULTS, ns_precision=0)), 2, label="zero-grads")
+
+
 def test_tail_only_table():
     """No Muon matrix at all: only the AdamW kernel runs (fp32 and bf16
     vectors, a scalar, a forced-AdamW matrix), over three steps of bias
