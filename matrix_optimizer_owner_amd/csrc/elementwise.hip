@@ -30,10 +30,10 @@ struct MomentumArgs {
     int nesterov;
 };
 
-// Eight consecutive momentum elements (fp32, or bf16 bits in uint16_t):
-// one raw vector load, unpacked to fp32.
-template <typename MT> struct Mom8;
-template <> struct Mom8<float> {
+// Eight consecutive elements (fp32, or bf16 bits in uint16_t) of the
+// momentum or of an AdamW tensor: one raw vector load, unpacked to fp32.
+template <typename MT> struct Raw8;
+template <> struct Raw8<float> {
     struct raw { float4 a, b; };
     __device__ static raw load(const float* p) {
         const float4* q = reinterpret_cast<const float4*>(p);
@@ -44,7 +44,7 @@ template <> struct Mom8<float> {
         v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
     }
 };
-template <> struct Mom8<uint16_t> {
+template <> struct Raw8<uint16_t> {
     using raw = uint4;
     __device__ static raw load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
     __device__ static void get(const raw& r, float (&v)[8]) {
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
         // compiler cannot know that), then the arithmetic and the stores
         uint4 graw[SUB];
         float4 gf[SUB][2];
-        typename Mom8<MT>::raw mf[SUB];
+        typename Raw8<MT>::raw mf[SUB];
         MT* mrow = mom + int64_t(r0) * C + c0;
         const int ld4 = C / 4;
         if (d.dtype == kBF16) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < SUB; ++i) mf[i] = Mom8<MT>::load(mrow + int64_t(i) * C);
+        for (int i = 0; i < SUB; ++i) mf[i] = Raw8<MT>::load(mrow + int64_t(i) * C);
 #pragma unroll
         for (int i = 0; i < SUB; ++i) {
             float gv[8];
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
                 gv[4] = gf[i][1].x; gv[5] = gf[i][1].y; gv[6] = gf[i][1].z; gv[7] = gf[i][1].w;
             }
             float mv[8];
-            Mom8<MT>::get(mf[i], mv);
+            Raw8<MT>::get(mf[i], mv);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 mv[k] = __builtin_fmaf(a.beta, mv[k], gv[k]);
@@ -259,20 +259,10 @@ struct AdamArgs {
 // Eight consecutive parameter / gradient elements (fp32, or bf16 rounded to
 // nearest-even on store) as 16-byte vectors.
 __device__ __forceinline__ void load8(const uint8_t* base, int dtype, int64_t i, float (&v)[8]) {
-    if (dtype == kBF16) {
-        const uint4 r = *reinterpret_cast<const uint4*>(base + 2 * i);
-        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(u[k] << 16);
-            v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
-        }
-    } else {
-        const float4* p = reinterpret_cast<const float4*>(base + 4 * i);
-        const float4 x = p[0], y = p[1];
-        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-    }
+    if (dtype == kBF16)
+        Raw8<uint16_t>::get(Raw8<uint16_t>::load(reinterpret_cast<const uint16_t*>(base) + i), v);
+    else
+        Raw8<float>::get(Raw8<float>::load(reinterpret_cast<const float*>(base) + i), v);
 }
 __device__ __forceinline__ void store8(uint8_t* base, int dtype, int64_t i, const float (&v)[8]) {
     if (dtype == kBF16)
