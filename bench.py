@@ -207,8 +207,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the owner step on one GPU; the owner step has no cross-GPU work, and runs with "
-              "--gpus above 1 are not supported by this build.", file=sys.stderr)
+        print("bench.py measures the owner step on one GPU (the step has no cross-GPU work); "
+              "--gpus above 1 is not supported.", file=sys.stderr)
         return 2
     if args.copy_probe_gib > 0:
         copy_probe(args.copy_probe_gib)

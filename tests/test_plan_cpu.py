@@ -7,6 +7,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -243,3 +244,11 @@ def test_step_argument_checks_without_gpu():
     assert st(events=(1, 2)) == 1               # too few events
     empty = _plan([B.TableEntry(0, 0, 8)])
     empty.step(0, 0, 0, 0, 0, 0)                # nothing to do: returns OK without touching HIP
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU's owner step; --gpus 2 exits with status 2
+    and a message, before touching any GPU."""
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU" in res.stderr, (res.returncode, res.stderr)
