@@ -77,7 +77,9 @@ def test_two_iterations_sketch_full_size(cfg):
     wl = W.config(cfg)
     run = DeviceRun(wl, {"ns_steps": 2})
     hp = oracle_hparams(run.hp)
-    idxs = pick(wl, 4)
+    # every distinct shape of the mixed set (28: four min dimensions, aspect
+    # 1-8, tall and wide), four spread over cost elsewhere
+    idxs = pick(wl, 1000 if cfg == 3 else 4)
     say(f"[sketch cfg{cfg}] {wl.name}: checking {[(wl.specs[i].rows, wl.specs[i].cols) for i in idxs]}")
     run.fill(1, params_too=True)
     snap = run.snapshot_entries(idxs)
