@@ -335,6 +335,28 @@ def main() -> int:
     copy_gbs = 2.0 * (1 << 30) * 5 / (time.perf_counter() - c0) / 1e9
     del cbuf, csrc, cdst
 
+    # bf16 MFMA rate this GPU sustains, measured live on register-only MFMA
+    # loops (one block of 4 waves per CU, about 60 ms each, long enough for the
+    # clock to settle): the clock under load depends on the operand data, so
+    # Gaussian bf16 (the contractions' kind of data) and zeros.  The operands
+    # stay in registers (16 fragments per lane), so fewer operand bits toggle
+    # than in a contraction streaming fresh fragments: an upper bound on what
+    # a contraction can sustain on such data.
+    mfma_ceiling = None
+    if prec == "bf16":
+        ops = torch.randn(1 << 22, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        sink = torch.empty(256 * 4, dtype=torch.float32, device=dev)
+        mfma_ceiling = {}
+        for name, buf in (("gaussian_bf16", ops), ("zeros", torch.zeros_like(ops))):
+            B.probe_mfma_bf16(buf.data_ptr(), buf.numel() * 2, 256, 2000, sink.data_ptr(), stream)  # warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fl = B.probe_mfma_bf16(buf.data_ptr(), buf.numel() * 2, 256, 100000, sink.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            mfma_ceiling[name + "_tflops"] = round(fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del ops, sink
+
     roofline = None
     if not specs and adam_ms:
         # tail-only buffer: the AdamW kernel is the step (28 B per fp32 element)
@@ -347,6 +369,9 @@ def main() -> int:
         ach = per_launch[dom] / (avg * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4), "traffic": measured_traffic(wl.name, prec, dom),
+                    "measured_mfma_ceiling": mfma_ceiling,
+                    "frac_of_measured_ceiling": (round(ach / mfma_ceiling["gaussian_bf16_tflops"], 4)
+                                                 if mfma_ceiling else None),
                     "kernel": f"k_ns_gemm ({dom} phase)", "avg_launch_ms": round(avg, 4),
                     "algorithmic_flop_per_launch": per_launch[dom]}
 

@@ -285,6 +285,20 @@ mfsdp_status mfsdp_owner_scatter(mfsdp_plan_t plan, const void* const* tensors, 
                                  uint64_t state_bytes);
 
 /* Static description of a status code. */
+/* Measurement support (not part of the step): enqueue on `stream` a
+ * register-only loop of bf16 MFMAs (v_mfma_f32_32x32x16_bf16, fp32
+ * accumulate) over `blocks` blocks of 4 waves, each wave running `iters`
+ * iterations of 32 MFMAs on 16 operand fragments per lane taken from
+ * `operands` (device memory, operand_bytes >= 1024, a multiple of 16,
+ * 16-byte aligned; read only).  The MFMA clock depends on the operand data,
+ * so with the contractions' own kind of data (Gaussian bf16) the elapsed
+ * time gives the rate the part sustains for them, as opposed to the
+ * published dense peak.  sink: device, blocks * 4 floats, written.  *flops
+ * (optional) receives the FLOPs enqueued.  The caller times the launch (for
+ * example with events on `stream`).  Errors: INVALID_ARGUMENT, HIP. */
+mfsdp_status mfsdp_probe_mfma_bf16(const void* operands, uint64_t operand_bytes, int32_t blocks, int32_t iters,
+                                   float* sink, void* stream, double* flops);
+
 const char* mfsdp_status_string(mfsdp_status status);
 
 /* Thread-local description of the last error on this thread ("" if none). */

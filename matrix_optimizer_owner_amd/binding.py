@@ -82,7 +82,7 @@ EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
     "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
     "mfsdp_owner_partition", "mfsdp_owner_gather", "mfsdp_owner_scatter", "mfsdp_status_string",
-    "mfsdp_last_error_message",
+    "mfsdp_last_error_message", "mfsdp_probe_mfma_bf16",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -113,6 +113,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vpp = ctypes.POINTER(ctypes.c_void_p)
     lib.mfsdp_owner_gather.argtypes = [P, P, ctypes.c_uint64, P, ctypes.c_uint64, vpp, vpp, vpp]
     lib.mfsdp_owner_scatter.argtypes = [P, vpp, vpp, vpp, P, ctypes.c_uint64, P, ctypes.c_uint64]
+    lib.mfsdp_probe_mfma_bf16.argtypes = [P, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, P, P,
+                                          ctypes.POINTER(ctypes.c_double)]
     lib.mfsdp_status_string.argtypes = [ctypes.c_int]
     lib.mfsdp_status_string.restype = ctypes.c_char_p
     lib.mfsdp_last_error_message.argtypes = []
@@ -286,3 +288,13 @@ def owner_partition(shapes: Sequence[tuple], dtypes: Sequence[int], n_owners: in
                      [place[i].offset for i in range(n)], [place[i].cost for i in range(n)],
                      [place[i].mem_bytes for i in range(n)], list(oc[:n_owners]), list(om[:n_owners]),
                      list(ob[:n_owners]))
+
+
+def probe_mfma_bf16(operands: int, operand_bytes: int, blocks: int, iters: int, sink: int, stream: int = 0) -> float:
+    """Enqueue the register-only bf16 MFMA loop (mfsdp_probe_mfma_bf16) on
+    `stream` over device operands; returns the FLOPs enqueued."""
+    lib = load()
+    flops = ctypes.c_double()
+    _check(lib.mfsdp_probe_mfma_bf16(ctypes.c_void_p(operands), operand_bytes, blocks, iters, ctypes.c_void_p(sink),
+                                     ctypes.c_void_p(stream), ctypes.byref(flops)))
+    return flops.value

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmfsdp.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["plan.cpp", "owner_planner.cpp", "checkpoint.cpp", "step.hip", "elementwise.hip", "ns_gemm.hip"]
+SOURCES = ["plan.cpp", "owner_planner.cpp", "checkpoint.cpp", "step.hip", "elementwise.hip", "ns_gemm.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -252,3 +252,16 @@ def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr, (res.returncode, res.stderr)
+
+
+def test_mfma_probe_argument_checks_without_gpu(lib):
+    """The MFMA-rate probe validates its arguments before any launch."""
+    sink = (ctypes.c_float * 4)()
+    ops = (ctypes.c_uint8 * 2048)()
+    def status(operands, nbytes, blocks, iters, snk):
+        return lib.mfsdp_probe_mfma_bf16(operands, nbytes, blocks, iters, snk, None, None)
+    assert status(None, 2048, 1, 1, ctypes.cast(sink, ctypes.c_void_p)) == 1
+    assert status(ctypes.cast(ops, ctypes.c_void_p), 2048, 1, 1, None) == 1
+    assert status(ctypes.cast(ops, ctypes.c_void_p), 512, 1, 1, ctypes.cast(sink, ctypes.c_void_p)) == 1
+    assert status(ctypes.cast(ops, ctypes.c_void_p), 2048, 0, 1, ctypes.cast(sink, ctypes.c_void_p)) == 1
+    assert status(ctypes.cast(ops, ctypes.c_void_p), 2048, 1, 0, ctypes.cast(sink, ctypes.c_void_p)) == 1
