@@ -12,7 +12,8 @@
  * that live in one flat parameter buffer, and one call that updates all of
  * them.
  *
- * Per Muon matrix W (rows x cols), gradient G, fp32 momentum M:
+ * Per Muon matrix W (rows x cols), gradient G, momentum M (fp32, or bf16 by
+ * hparams.momentum_dtype):
  *   M <- beta*M + G;  U <- G + beta*M (Nesterov) or U <- M;
  *   X <- U / (||U||_F + eps), taken in the wide orientation (tall -> U^T);
  *   ns_steps times: A = X X^T;  B = b*A + c*A*A;  X <- a*X + B*X;
