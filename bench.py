@@ -98,8 +98,10 @@ def cpu_baseline(wl, budget_s: float):
         m, n = min(s.rows, s.cols), max(s.rows, s.cols)
         return steps * (4.0 * m * m * n + 2.0 * m ** 3)
 
-    # one matrix of each distinct shape, cheapest first, within the budget
-    # (estimated at 0.3 TFLOP/s of fp64 until the first measurement)
+    # one matrix of each distinct shape, cheapest first, while the estimated
+    # total stays within 1.5x the budget (the rate estimated at 0.3 TFLOP/s of
+    # fp64 until the first measurement), so that a workload of few, large
+    # shapes still gets a sample of about the budget
     seen, sample = set(), []
     for s in sorted(specs, key=flops):
         key = (s.rows, s.cols)
@@ -110,7 +112,7 @@ def cpu_baseline(wl, budget_s: float):
     t_used, f_used, names = 0.0, 0.0, []
     rate = 0.3e12
     for s in sample:
-        if t_used > 0 and t_used + flops(s) / rate > budget_s:
+        if t_used > 0 and t_used + flops(s) / rate > 1.5 * budget_s:
             continue
         w = rng.standard_normal((s.rows, s.cols)) * 0.02
         g = rng.standard_normal((s.rows, s.cols)) * s.grad_std
