@@ -335,7 +335,20 @@ def main() -> int:
         cdst.copy_(csrc)
     torch.cuda.synchronize()
     copy_gbs = 2.0 * (1 << 30) * 5 / (time.perf_counter() - c0) / 1e9
-    del cbuf, csrc, cdst
+    # streaming rates with the library's probe (16-byte accesses over 1 GiB):
+    # read only, write only, copy (the read/write mix of the elementwise phases)
+    hbm = {}
+    hsink = torch.empty(8192, dtype=torch.float32, device=dev)
+    for name, mode, moved in (("read", 0, 1), ("write", 1, 1), ("copy", 2, 2)):
+        B.probe_hbm(cdst.data_ptr(), csrc.data_ptr(), 1 << 30, mode, hsink.data_ptr(), stream)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            B.probe_hbm(cdst.data_ptr(), csrc.data_ptr(), 1 << 30, mode, hsink.data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        hbm[name + "_gbs"] = round(moved * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del cbuf, csrc, cdst, hsink
 
     # bf16 MFMA rate this GPU sustains, measured live on register-only MFMA
     # loops (one block of 4 waves per CU, about 60 ms each, long enough for the
@@ -409,6 +422,7 @@ def main() -> int:
                         "momentum_frac_hbm": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if mom_ms else None,
                         "momentum_bytes_per_elem": round(k1_bytes / muon_el, 3) if muon_el else None,
                         "copy_ceiling_gbs": round(copy_gbs, 1),
+                        "hbm_stream_probe": hbm,
                         "momentum_frac_copy_ceiling": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / copy_gbs, 4) if mom_ms else None,
                         "adamw_gbs": round(tail_bytes / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},
         "roofline": roofline,

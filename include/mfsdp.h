@@ -300,6 +300,17 @@ mfsdp_status mfsdp_owner_scatter(mfsdp_plan_t plan, const void* const* tensors, 
 mfsdp_status mfsdp_probe_mfma_bf16(const void* operands, uint64_t operand_bytes, int32_t blocks, int32_t iters,
                                    float* sink, void* stream, double* flops);
 
+/* Measurement support (not part of the step): enqueue on `stream` one pass
+ * of 16-byte accesses over `bytes` of device memory: mode 0 reads src, mode
+ * 1 writes dst, mode 2 copies src to dst (as many bytes read as written, the
+ * mix of the elementwise phases).  2048 blocks of 256 threads, each walking
+ * contiguous 32 KB chunks with 8 accesses in flight per thread.  The caller
+ * times the launch; the
+ * bytes moved are `bytes` (modes 0, 1) or 2 * bytes (mode 2).  sink: device,
+ * 8192 floats, written.  Errors: INVALID_ARGUMENT (mode, NULL buffer, bytes
+ * not a nonzero multiple of 16, misaligned buffer), HIP. */
+mfsdp_status mfsdp_probe_hbm(void* dst, const void* src, uint64_t bytes, int32_t mode, float* sink, void* stream);
+
 const char* mfsdp_status_string(mfsdp_status status);
 
 /* Thread-local description of the last error on this thread ("" if none). */

@@ -82,7 +82,7 @@ EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
     "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
     "mfsdp_owner_partition", "mfsdp_owner_gather", "mfsdp_owner_scatter", "mfsdp_status_string",
-    "mfsdp_last_error_message", "mfsdp_probe_mfma_bf16",
+    "mfsdp_last_error_message", "mfsdp_probe_mfma_bf16", "mfsdp_probe_hbm",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -115,6 +115,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_owner_scatter.argtypes = [P, vpp, vpp, vpp, P, ctypes.c_uint64, P, ctypes.c_uint64]
     lib.mfsdp_probe_mfma_bf16.argtypes = [P, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, P, P,
                                           ctypes.POINTER(ctypes.c_double)]
+    lib.mfsdp_probe_hbm.argtypes = [P, P, ctypes.c_uint64, ctypes.c_int32, P, P]
     lib.mfsdp_status_string.argtypes = [ctypes.c_int]
     lib.mfsdp_status_string.restype = ctypes.c_char_p
     lib.mfsdp_last_error_message.argtypes = []
@@ -298,3 +299,10 @@ def probe_mfma_bf16(operands: int, operand_bytes: int, blocks: int, iters: int, 
     _check(lib.mfsdp_probe_mfma_bf16(ctypes.c_void_p(operands), operand_bytes, blocks, iters, ctypes.c_void_p(sink),
                                      ctypes.c_void_p(stream), ctypes.byref(flops)))
     return flops.value
+
+
+def probe_hbm(dst: int, src: int, nbytes: int, mode: int, sink: int, stream: int = 0) -> None:
+    """Enqueue one streaming pass (mfsdp_probe_hbm): mode 0 read, 1 write,
+    2 copy."""
+    _check(load().mfsdp_probe_hbm(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, mode, ctypes.c_void_p(sink),
+                                  ctypes.c_void_p(stream)))

@@ -73,3 +73,64 @@ extern "C" mfsdp_status mfsdp_probe_mfma_bf16(const void* operands, uint64_t ope
     if (flops) *flops = double(blocks) * kProbeWaves * double(iters) * 32.0 * (32.0 * 32.0 * 16.0 * 2.0);
     return MFSDP_OK;
 }
+
+// ---------------------------------------------------------------------------
+// HBM streaming rates: read only, write only, and copy (half read, half
+// written), 16-byte accesses: each block walks contiguous 32 KB chunks
+// (chunk b, b + blocks, ...), each thread 8 accesses in flight, a wave's
+// access covering 1 KB of consecutive bytes.  The elementwise phases move as many bytes in as out (momentum:
+// 6 B read and 6 B written per bf16 element), so the copy rate is their
+// ceiling on this part, below the published 8 TB/s.
+namespace mfsdp {
+namespace {
+
+constexpr int kHbmBlocks = 2048, kHbmThreads = 256, kHbmUnroll = 8;
+
+__global__ __launch_bounds__(kHbmThreads) void k_probe_hbm(u32x4_t* dst, const u32x4_t* src, int64_t n, int mode,
+                                                            float* sink) {
+    constexpr int64_t kChunk = int64_t(kHbmThreads) * kHbmUnroll;  // 16-byte words per block chunk
+    const int64_t t = threadIdx.x;
+    uint32_t acc = 0;
+    for (int64_t base = int64_t(blockIdx.x) * kChunk; base < n; base += int64_t(gridDim.x) * kChunk) {
+        u32x4_t v[kHbmUnroll];
+#pragma unroll
+        for (int u = 0; u < kHbmUnroll; ++u) {
+            const int64_t i = base + u * kHbmThreads + t;
+            if (mode != 1 && i < n) v[u] = src[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kHbmUnroll; ++u) {
+            const int64_t i = base + u * kHbmThreads + t;
+            if (i >= n) continue;
+            if (mode == 0)
+                acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+            else if (mode == 1)
+                dst[i] = u32x4_t{uint32_t(i), 0u, 0u, 0u};
+            else
+                dst[i] = v[u];
+        }
+    }
+    // keeps the reads live: one value per wave
+    const float f = float(acc & 0xffffu);
+    const float s = wave_sum(f);
+    if ((threadIdx.x & 63) == 0) sink[(blockIdx.x * kHbmThreads + threadIdx.x) / 64] = s;
+}
+
+}  // namespace
+}  // namespace mfsdp
+
+extern "C" mfsdp_status mfsdp_probe_hbm(void* dst, const void* src, uint64_t bytes, int32_t mode, float* sink,
+                                        void* stream) {
+    clear_error();
+    if (mode < 0 || mode > 2) return fail(MFSDP_ERR_INVALID_ARGUMENT, "mode must be 0 (read), 1 (write) or 2 (copy)");
+    if (!sink || (mode != 1 && !src) || (mode != 0 && !dst))
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL buffer");
+    if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(dst) % 16 != 0)
+        return fail(MFSDP_ERR_INVALID_ARGUMENT, "bytes a nonzero multiple of 16, buffers 16-byte aligned");
+    k_probe_hbm<<<dim3(kHbmBlocks), dim3(kHbmThreads), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<u32x4_t*>(dst), static_cast<const u32x4_t*>(src), int64_t(bytes / 16), mode, sink);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MFSDP_ERR_HIP, std::string("probe launch: ") + hipGetErrorString(e));
+    return MFSDP_OK;
+}

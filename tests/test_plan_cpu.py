@@ -265,3 +265,15 @@ def test_mfma_probe_argument_checks_without_gpu(lib):
     assert status(ctypes.cast(ops, ctypes.c_void_p), 512, 1, 1, ctypes.cast(sink, ctypes.c_void_p)) == 1
     assert status(ctypes.cast(ops, ctypes.c_void_p), 2048, 0, 1, ctypes.cast(sink, ctypes.c_void_p)) == 1
     assert status(ctypes.cast(ops, ctypes.c_void_p), 2048, 1, 0, ctypes.cast(sink, ctypes.c_void_p)) == 1
+
+
+def test_hbm_probe_argument_checks_without_gpu(lib):
+    sink = (ctypes.c_float * 8192)()
+    buf = (ctypes.c_uint8 * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    s = ctypes.cast(sink, ctypes.c_void_p)
+    assert lib.mfsdp_probe_hbm(p, p, 64, 3, s, None) == 1      # mode
+    assert lib.mfsdp_probe_hbm(p, None, 64, 0, s, None) == 1   # read without src
+    assert lib.mfsdp_probe_hbm(None, p, 64, 1, s, None) == 1   # write without dst
+    assert lib.mfsdp_probe_hbm(p, p, 60, 2, s, None) == 1      # not a multiple of 16
+    assert lib.mfsdp_probe_hbm(p, p, 64, 2, None, None) == 1   # no sink

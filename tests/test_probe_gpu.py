@@ -23,3 +23,29 @@ def test_probe_sums_are_exact():
         torch.cuda.synchronize()
         assert flops == 64 * 4 * iters * 32 * 32 * 32 * 16 * 2
         assert bool((sink == want).all()), (fill, sink[:4].tolist())
+
+
+def test_hbm_probe_copies_and_writes():
+    """The streaming probe's copy mode copies, its write mode writes its
+    pattern (element i of 16-byte words: i, 0, 0, 0), its read mode leaves
+    memory alone."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    n = (1 << 20) + 48  # not a multiple of the grid: the bounds of the last pass
+    src = torch.randint(0, 2 ** 31 - 1, (n,), dtype=torch.int32, device=dev)
+    dst = torch.zeros(n, dtype=torch.int32, device=dev)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+    B.probe_hbm(dst.data_ptr(), src.data_ptr(), n * 4, 2, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    before = src.clone()
+    B.probe_hbm(0, src.data_ptr(), n * 4, 0, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert torch.equal(src, before)
+    B.probe_hbm(dst.data_ptr(), 0, n * 4, 1, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    words = dst.view(-1, 4)
+    assert torch.equal(words[:, 0], torch.arange(n // 4, dtype=torch.int32, device=dev))
+    assert int(words[:, 1:].abs().sum()) == 0
