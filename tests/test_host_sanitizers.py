@@ -1,0 +1,74 @@
+"""Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
+
+The planner (plan.cpp) is built with g++ (no device code) together with the
+plan checker and run on every workload table, the seeded random tables,
+the largest accepted matrices, a tail-only and an empty table: no sanitizer
+report, and every plan passes the checker's invariants.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+from matrix_optimizer_owner_amd import workloads as W
+from tests.test_plan_cpu import _max_size, _table_text
+from tests.test_random_shapes_gpu import random_table
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "matrix_optimizer_owner_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def checker_sanitized(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("san") / "plan_check_san")
+    flags = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "plan.cpp"), os.path.join(ROOT, "tests", "plan_check.cpp"), "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip("sanitizer runtime not available: " + res.stderr[-300:])
+    return exe
+
+
+def _tables():
+    out = [(f"c{i}", W.config(i)) for i in range(len(W.CONFIGS))]
+    out += [(f"random{s}", random_table(s, p)) for s, p in ((21, 0), (22, 0), (23, 1))]
+    out += [("max_wide", _max_size(32500, 32700)), ("max_tall", _max_size(32700, 32500)),
+            ("small_ragged", W.small_ragged()),
+            ("empty", W.Workload("empty", [], seed=0, hparams=dict(W.MUON_DEFAULTS)))]
+    return out
+
+
+def test_planner_clean_under_sanitizers(checker_sanitized):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    for name, wl in _tables():
+        res = subprocess.run([checker_sanitized], input=_table_text(wl), capture_output=True, text=True, env=env,
+                             timeout=300)
+        assert res.returncode == 0 and res.stdout.startswith("OK"), (name, res.stdout[-500:], res.stderr[-2000:])
+        assert "runtime error" not in res.stderr and "Sanitizer" not in res.stderr, (name, res.stderr[-2000:])
+
+
+def test_planner_and_checkpoint_copies_clean_under_sanitizers(tmp_path):
+    """Owner partitions of seeded random tensor lists, every owner's plan,
+    and bit-exact scatter/gather round trips of random bytes (fp32 and bf16
+    momentum), plus invalid-argument calls, under the sanitizers."""
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "host_check_san")
+    srcs = [os.path.join(CSRC, f) for f in ("plan.cpp", "owner_planner.cpp", "checkpoint.cpp")]
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, os.path.join(ROOT, "tests", "host_check.cpp"),
+           "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        pytest.skip("sanitizer runtime not available: " + res.stderr[-300:])
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0 and res.stdout.startswith("OK"), (res.stdout[-500:], res.stderr[-2000:])
+    assert "runtime error" not in res.stderr and "Sanitizer" not in res.stderr, res.stderr[-2000:]
