@@ -931,7 +931,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             group_k(F0{}, FIRST, fa1, fb1, LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
             if constexpr (kFoldAX && !first)
                 if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
-            group_k(FIRST, F0{}, fa0, fb0, NR + LP, NF, [&](int t) {
+            // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
+            // run of LP loads after group 1's reads they overfilled the
+            // texture-address queues (the queue-full counters read about half
+            // of the busy cycles) and held up the MFMAs queued behind them
+            constexpr int LP1 = LP / 2, LP2 = LP - LP1;
+            group_k(FIRST, F0{}, fa0, fb0, NR + LP1, NF, [&](int t) {
                 if (t < NR)
                     read_one(t, oP, oQ, 1, fa1, fb1);
                 else
@@ -941,7 +946,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                 if (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
             if constexpr (kFoldAX)
                 if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
-            group_k(F0{}, F0{}, fa1, fb1, NR, NF, [&](int t) { read_one(t, oP, oQ, 2, fa0, fb0); });
+            group_k(F0{}, F0{}, fa1, fb1, NR + LP2, NF, [&](int t) {
+                if (t < NR)
+                    read_one(t, oP, oQ, 2, fa0, fb0);
+                else
+                    load_one(true, kp, oPn, LP1 + t - NR);
+            });
             if constexpr (kFoldAX)
                 if (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
             group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
