@@ -14,7 +14,8 @@ after step t-1, read back from the device.  Criteria (per matrix / tensor):
 * momentum: relative error <= 1e-6 (one fp32 rounding); stored in bf16
   (momentum_dtype): within half a bf16 ulp of the oracle's value plus 1e-6
   of the larger operand (beta m or g);
-* AdamW tail: relative Frobenius error <= 1e-6 on W, m and v (fp32 tails);
+* AdamW tail: relative Frobenius error <= 1e-6 on W, m and v (fp32 tails;
+  for W relative to the larger of the result and the update's operands);
   bf16 tails: within half a bf16 ulp of the oracle's W plus 1e-6 of the
   larger operand of the update (the fp32 error before the rounding).
 """
@@ -266,7 +267,15 @@ def check_step(run: DeviceRun, before, after, step: int, entries=None, sigma=Tru
                 if not d <= 1e-6:
                     rep.failures.append(f"AdamW {nm} relative error {d:.3e} > 1e-6")
             if s.dtype == "f32":
-                d = np.linalg.norm(w1 - w_orc) / max(np.linalg.norm(w_orc), 1e-300)
+                # relative to the larger of the result and the update's
+                # operands (W and lr m_hat / (sqrt(v_hat) + eps)): for a
+                # tensor whose W and step nearly cancel (a scalar, say) the
+                # result-relative error of exact fp32 arithmetic is unbounded
+                m_hat = m_orc / (1.0 - hp.adam_beta1 ** step)
+                v_hat = v_orc / (1.0 - hp.adam_beta2 ** step)
+                step_term = hp.adam_lr * np.abs(m_hat) / (np.sqrt(v_hat) + hp.adam_eps)
+                ref = max(np.linalg.norm(w_orc), np.linalg.norm(w0), np.linalg.norm(step_term), 1e-300)
+                d = np.linalg.norm(w1 - w_orc) / ref
                 rep.metrics["adam_w_rel"] = float(d)
                 if not d <= 1e-6:
                     rep.failures.append(f"AdamW W relative error {d:.3e} > 1e-6")

@@ -50,7 +50,8 @@ def random_table(seed: int, precision: int) -> W.Workload:
     return _Packed(f"random-table-s{seed}-p{precision}", sp, seed, dict(W.MUON_DEFAULTS, ns_precision=precision), gaps)
 
 
-@pytest.mark.parametrize("seed,precision,tile", [(21, 0, None), (22, 0, "256"), (23, 1, None)])
+@pytest.mark.parametrize("seed,precision,tile", [(21, 0, None), (22, 0, "256"), (23, 1, None), (24, 0, "256"),
+                                                 (25, 0, "256"), (26, 1, "256"), (27, 0, "128")])
 def test_random_tables(seed, precision, tile, monkeypatch):
     if tile:
         monkeypatch.setenv("MFSDP_TILE", tile)
