@@ -178,11 +178,11 @@ def adamw_tail_probe() -> Workload:
     return Workload("adamw-tail-64x4Mi-fp32", sp, seed=7, hparams=dict(MUON_DEFAULTS, ns_precision=0))
 
 
-CONFIGS = [single_fp32, gpt2_small, llama3_8b_share, mixed_stress, llama3_70b_share, adamw_tail_probe]
+WORKLOADS = [single_fp32, gpt2_small, llama3_8b_share, mixed_stress, llama3_70b_share, adamw_tail_probe]
 
 
 def config(i: int) -> Workload:
-    return CONFIGS[i]()
+    return WORKLOADS[i]()
 
 
 def small_ragged(seed: int = 5, precision: int = 0) -> Workload:

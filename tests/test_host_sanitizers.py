@@ -37,7 +37,7 @@ def checker_sanitized(tmp_path_factory):
 
 
 def _tables():
-    out = [(f"c{i}", W.config(i)) for i in range(len(W.CONFIGS))]
+    out = [(f"c{i}", W.config(i)) for i in range(len(W.WORKLOADS))]
     out += [(f"random{s}", random_table(s, p)) for s, p in ((21, 0), (22, 0), (23, 1))]
     out += [("max_wide", _max_size(32500, 32700)), ("max_tall", _max_size(32700, 32500)),
             ("small_ragged", W.small_ragged()),
