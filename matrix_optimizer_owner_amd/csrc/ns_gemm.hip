@@ -25,10 +25,10 @@
 // phases with too few large tiles to fill the chip.  Operands reach LDS by
 // direct global->LDS loads in 128-byte rows (64 bf16 or 32 fp32 of the
 // contraction index per stage) into split stage rings (3 slots for P, 2 for
-// Q).  bf16 on 256 tiles runs a locked instruction schedule (MFMAs, fragment
-// reads and loads interleaved in a fixed order, over stage pairs) and, in
-// the update phases, adds a X through identity-fragment MFMAs; the other
-// kernels run a compiler-scheduled loop.  Operands that are contiguous along
+// Q).  bf16 runs a locked instruction schedule (MFMAs, fragment reads and
+// loads interleaved in a fixed order, over stage pairs) and, in the update
+// phases on 256 tiles, adds a X through identity-fragment MFMAs; fp32 runs a
+// compiler-scheduled loop.  Operands that are contiguous along
 // the contraction are read back with 16-byte fragment reads; the Gram's
 // K-major X^T is read back with the transposing LDS read
 // (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
@@ -585,16 +585,18 @@ __device__ __forceinline__ void dma16_unseen(i32x4_t rs, uint32_t lds_addr, uint
 }
 #pragma clang diagnostic pop
 
-// Locked schedule: one wave per SIMD (4 waves of 128 x 128 on 256 tiles,
-// bf16) issuing a fixed instruction order.  Each of the stage's four groups
-// of 16 MFMAs carries its side work between the MFMAs: the next sub-step's
-// fragment reads and the stage's direct-to-LDS loads.  Scheduling fences
-// keep the compiler from regrouping them (left to itself it moves every LDS
-// read next to its first use and then waits for it).  The other kernels
-// (fp32, 128 tiles) run the compiler-scheduled loop over the same rings.
+// Locked schedule (bf16): 4 waves issuing a fixed instruction order, one
+// per SIMD with 128 x 128 each on 256 tiles, 64 x 64 each on 128 tiles (two
+// blocks per CU).  Each of the stage's four groups of MFMAs (16 on 256
+// tiles, 4 on 128) carries its side work between the MFMAs: the next
+// sub-step's fragment reads and the stage's direct-to-LDS loads.
+// Scheduling fences keep the compiler from regrouping them (left to itself
+// it moves every LDS read next to its first use and then waits for it); on
+// 128 tiles this took the Gram of a 48-matrix m = 768 buffer from 0.129 to
+// 0.110 ms.  fp32 runs the compiler-scheduled loop over the same rings.
 template <typename T, int PHASE, int BT, int NW>
 struct Lock4 {
-    static constexpr bool value = sizeof(T) == 2 && BT == 256 && NW == 4;
+    static constexpr bool value = sizeof(T) == 2 && NW == 4;
 };
 
 // LDS of the block: the main loop's 5 operand stages; the epilogues reuse
@@ -616,7 +618,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     // the Gram's operands are K-major (X^T rows are the contraction index)
     constexpr bool KM = PHASE == kGram;
     // the update phases of the locked loop add a X inside the main loop
-    constexpr bool kFoldAX = Lock4<T, PHASE, BT, NW>::value && (PHASE == kUpdate || PHASE == kFinal);
+    // (256 tiles only: the fold's placement assumes each wave's 128 output
+    // rows span one stage pair of the contraction; on 128 tiles the
+    // epilogue adds a X)
+    constexpr bool kFoldAX = Lock4<T, PHASE, BT, NW>::value && BT == 256 && (PHASE == kUpdate || PHASE == kFinal);
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
@@ -1098,9 +1103,9 @@ __global__ __launch_bounds__(64 * NW, (BT == 256 ? 1 : 2)) void k_ns_gemm(GemmAr
     gemm_tile<T, PHASE, BT, NW>(a, blockIdx.x, lds_raw);
 }
 
-// 256 tiles: 4 waves, one per SIMD, 128 x 128 each (the locked schedule for
-// bf16); two waves per SIMD with 128 x 64 each measured 4-12% slower per
-// phase.  128 tiles: 4 waves of 64 x 64, two blocks per CU.
+// 256 tiles: 4 waves, one per SIMD, 128 x 128 each; two waves per SIMD
+// with 128 x 64 each measured 4-12% slower per phase.  128 tiles: 4 waves
+// of 64 x 64, two blocks per CU.
 
 template <typename T, int PHASE>
 void launch_tiles(GemmArgs a, int n_tiles, int tile, hipStream_t stream) {
