@@ -896,17 +896,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I3 = std::integral_constant<int, 3>;
+        // DG: a diagonal tile of the Gram or the polynomial, whose P and Q
+        // stages hold the same rows of the same matrix: Q is not loaded and
+        // its fragments are read from P's slot.  The end-of-stage wait
+        // (all but the LP most recent loads) then waits for P of t + 1 alone.
+        auto run = [&](auto DG) {
+        constexpr bool dg = decltype(DG)::value;
 #pragma unroll
         for (int i = 0; i < LP; ++i) load_one(true, 0, 0, i);
+        if constexpr (!dg) {
 #pragma unroll
-        for (int i = 0; i < LP; ++i) load_one(false, 0, 3 * OPB, i);
+            for (int i = 0; i < LP; ++i) load_one(false, 0, 3 * OPB, i);
+        }
 #pragma unroll
         for (int i = 0; i < LP; ++i) load_one(true, 1 < KT ? 1 : KT - 1, OPB, i);
         waitcnt_seen<LP, 0>();
         __builtin_amdgcn_s_barrier();
         u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) read_one(r, 0, 3 * OPB, 0, fa0, fb0);
+        for (int r = 0; r < NR; ++r) read_one(r, 0, dg ? 0 : 3 * OPB, 0, fa0, fb0);
         __builtin_amdgcn_sched_barrier(0);
         int sp = 0, sq = 0;  // P and Q slots of stage kt
         // One stage; H = 0 / 1: first / second stage of a pair.  The wave's
@@ -923,7 +931,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             constexpr bool first = decltype(FIRST)::value;
             const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
             const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
-            const int oP = sp * OPB, oQ = (3 + sq) * OPB;
+            const int oP = sp * OPB, oQ = dg ? oP : (3 + sq) * OPB;
             const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
             if constexpr (kFoldAX && !first) {
                 if (fold_a) {
@@ -933,7 +941,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                         fold(I1{}, I1{}, fb1);  // sub-step 3 of the first stage of this pair
                 }
             }
-            group_k(F0{}, FIRST, fa1, fb1, LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
+            group_k(F0{}, FIRST, fa1, fb1, dg ? 0 : LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
             if constexpr (kFoldAX && !first)
                 if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
             // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
@@ -965,7 +973,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             sp = sp == 2 ? 0 : sp + 1;
             sq ^= 1;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, (3 + sq) * OPB, 0, fa0, fb0);
+            for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, dg ? sp * OPB : (3 + sq) * OPB, 0, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         };
         // (KT = K / KST is a multiple of 4: K is a multiple of 256)
@@ -979,6 +987,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
         mfmas(fa1, fb1);  // last sub-step of the last stage
         wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
+        };
+        if constexpr (PHASE == kGram || PHASE == kPoly) {
+            if (uni(int(tile.ti) - int(tile.tj)) == 0)
+                run(std::true_type{});
+            else
+                run(std::false_type{});
+        } else {
+            run(std::false_type{});
+        }
     } else {
         // Split rings: P's stage slots form a ring of 3 (byte offsets 0, OPB,
         // 2*OPB), Q's a ring of 2 (3*OPB, 4*OPB).  During stage t the block
