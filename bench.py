@@ -170,7 +170,7 @@ def cpu_baseline_tail(wl, hp, budget_s: float, cores: int):
 # for the kernel sources they were taken with.
 TRAFFIC = {
     # (workload, precision, phase): (sources sha256[:16], fetch bytes, write bytes)
-    ("llama3-8b-owner-share-4L", "bf16", "update"): ("f5bc46fbe646f0f3", 10177552656, 1744830464),
+    ("llama3-8b-owner-share-4L", "bf16", "update"): ("a99acbac78d04d8f", 10177552656, 1744830464),
 }
 TRAFFIC_SOURCES = ("matrix_optimizer_owner_amd/csrc/ns_gemm.hip", "matrix_optimizer_owner_amd/csrc/plan.cpp",
                    "matrix_optimizer_owner_amd/csrc/layout.h")

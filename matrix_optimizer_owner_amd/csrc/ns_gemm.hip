@@ -901,92 +901,92 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         // its fragments are read from P's slot.  The end-of-stage wait
         // (all but the LP most recent loads) then waits for P of t + 1 alone.
         auto run = [&](auto DG) {
-        constexpr bool dg = decltype(DG)::value;
+            constexpr bool dg = decltype(DG)::value;
 #pragma unroll
-        for (int i = 0; i < LP; ++i) load_one(true, 0, 0, i);
-        if constexpr (!dg) {
+            for (int i = 0; i < LP; ++i) load_one(true, 0, 0, i);
+            if constexpr (!dg) {
 #pragma unroll
-            for (int i = 0; i < LP; ++i) load_one(false, 0, 3 * OPB, i);
-        }
-#pragma unroll
-        for (int i = 0; i < LP; ++i) load_one(true, 1 < KT ? 1 : KT - 1, OPB, i);
-        waitcnt_seen<LP, 0>();
-        __builtin_amdgcn_s_barrier();
-        u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) read_one(r, 0, dg ? 0 : 3 * OPB, 0, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        int sp = 0, sq = 0;  // P and Q slots of stage kt
-        // One stage; H = 0 / 1: first / second stage of a pair.  The wave's
-        // rows rows_u .. rows_u+127 (rows_u a multiple of 128) are the
-        // contraction indices of the stage pair p0 = rows_u / (2*KST): the
-        // identity MFMAs of its 8 sub-steps sit at fixed places of the pair
-        // (sub-step u of stage 2*p0 + H covers rows 64*H + 16*u: MFMA block
-        // 2*H + u/2, offset 16*(u%2)), under the uniform flags fold_a
-        // (sub-step 3 of the previous stage, run first here) and fold_r (this
-        // stage's sub-steps 0-2).  FIRST: the tile's stage 0, with no
-        // deferred sub-step before it.
-        auto stage = [&](int kt, auto H, bool fold_a, bool fold_r, auto FIRST) {
-            constexpr int hh = decltype(H)::value;
-            constexpr bool first = decltype(FIRST)::value;
-            const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
-            const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
-            const int oP = sp * OPB, oQ = dg ? oP : (3 + sq) * OPB;
-            const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
-            if constexpr (kFoldAX && !first) {
-                if (fold_a) {
-                    if constexpr (hh == 0)
-                        fold(I3{}, I1{}, fb1);  // sub-step 3 of the second stage of the previous pair
-                    else
-                        fold(I1{}, I1{}, fb1);  // sub-step 3 of the first stage of this pair
-                }
+                for (int i = 0; i < LP; ++i) load_one(false, 0, 3 * OPB, i);
             }
-            group_k(F0{}, FIRST, fa1, fb1, dg ? 0 : LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
-            if constexpr (kFoldAX && !first)
-                if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
-            // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
-            // run of LP loads after group 1's reads they overfilled the
-            // texture-address queues (the queue-full counters read about half
-            // of the busy cycles) and held up the MFMAs queued behind them
-            constexpr int LP1 = LP / 2, LP2 = LP - LP1;
-            group_k(FIRST, F0{}, fa0, fb0, NR + LP1, NF, [&](int t) {
-                if (t < NR)
-                    read_one(t, oP, oQ, 1, fa1, fb1);
-                else
-                    load_one(true, kp, oPn, t - NR);
-            });
-            if constexpr (kFoldAX && first)
-                if (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
-            if constexpr (kFoldAX)
-                if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
-            group_k(F0{}, F0{}, fa1, fb1, NR + LP2, NF, [&](int t) {
-                if (t < NR)
-                    read_one(t, oP, oQ, 2, fa0, fb0);
-                else
-                    load_one(true, kp, oPn, LP1 + t - NR);
-            });
-            if constexpr (kFoldAX)
-                if (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
-            group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
+#pragma unroll
+            for (int i = 0; i < LP; ++i) load_one(true, 1 < KT ? 1 : KT - 1, OPB, i);
             waitcnt_seen<LP, 0>();
             __builtin_amdgcn_s_barrier();
-            sp = sp == 2 ? 0 : sp + 1;
-            sq ^= 1;
+            u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, dg ? sp * OPB : (3 + sq) * OPB, 0, fa0, fb0);
+            for (int r = 0; r < NR; ++r) read_one(r, 0, dg ? 0 : 3 * OPB, 0, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
-        };
-        // (KT = K / KST is a multiple of 4: K is a multiple of 256)
-        const int p0 = (row0 + (wave_u / S::WC) * S::WTM) / (2 * KST);  // uniform (wave_u)
-        stage(0, I0{}, false, kFoldAX && p0 == 0, F1{});
-        stage(1, I1{}, kFoldAX && p0 == 0, kFoldAX && p0 == 0, F0{});
-        for (int p = 1; p < KT / 2; ++p) {
-            stage(2 * p, I0{}, kFoldAX && p - 1 == p0, kFoldAX && p == p0, F0{});
-            stage(2 * p + 1, I1{}, kFoldAX && p == p0, kFoldAX && p == p0, F0{});
-        }
-        if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
-        mfmas(fa1, fb1);  // last sub-step of the last stage
-        wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
+            int sp = 0, sq = 0;  // P and Q slots of stage kt
+            // One stage; H = 0 / 1: first / second stage of a pair.  The wave's
+            // rows rows_u .. rows_u+127 (rows_u a multiple of 128) are the
+            // contraction indices of the stage pair p0 = rows_u / (2*KST): the
+            // identity MFMAs of its 8 sub-steps sit at fixed places of the pair
+            // (sub-step u of stage 2*p0 + H covers rows 64*H + 16*u: MFMA block
+            // 2*H + u/2, offset 16*(u%2)), under the uniform flags fold_a
+            // (sub-step 3 of the previous stage, run first here) and fold_r (this
+            // stage's sub-steps 0-2).  FIRST: the tile's stage 0, with no
+            // deferred sub-step before it.
+            auto stage = [&](int kt, auto H, bool fold_a, bool fold_r, auto FIRST) {
+                constexpr int hh = decltype(H)::value;
+                constexpr bool first = decltype(FIRST)::value;
+                const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
+                const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
+                const int oP = sp * OPB, oQ = dg ? oP : (3 + sq) * OPB;
+                const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
+                if constexpr (kFoldAX && !first) {
+                    if (fold_a) {
+                        if constexpr (hh == 0)
+                            fold(I3{}, I1{}, fb1);  // sub-step 3 of the second stage of the previous pair
+                        else
+                            fold(I1{}, I1{}, fb1);  // sub-step 3 of the first stage of this pair
+                    }
+                }
+                group_k(F0{}, FIRST, fa1, fb1, dg ? 0 : LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
+                if constexpr (kFoldAX && !first)
+                    if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
+                // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
+                // run of LP loads after group 1's reads they overfilled the
+                // texture-address queues (the queue-full counters read about half
+                // of the busy cycles) and held up the MFMAs queued behind them
+                constexpr int LP1 = LP / 2, LP2 = LP - LP1;
+                group_k(FIRST, F0{}, fa0, fb0, NR + LP1, NF, [&](int t) {
+                    if (t < NR)
+                        read_one(t, oP, oQ, 1, fa1, fb1);
+                    else
+                        load_one(true, kp, oPn, t - NR);
+                });
+                if constexpr (kFoldAX && first)
+                    if (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
+                if constexpr (kFoldAX)
+                    if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
+                group_k(F0{}, F0{}, fa1, fb1, NR + LP2, NF, [&](int t) {
+                    if (t < NR)
+                        read_one(t, oP, oQ, 2, fa0, fb0);
+                    else
+                        load_one(true, kp, oPn, LP1 + t - NR);
+                });
+                if constexpr (kFoldAX)
+                    if (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
+                group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
+                waitcnt_seen<LP, 0>();
+                __builtin_amdgcn_s_barrier();
+                sp = sp == 2 ? 0 : sp + 1;
+                sq ^= 1;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) read_one(r, sp * OPB, dg ? sp * OPB : (3 + sq) * OPB, 0, fa0, fb0);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // (KT = K / KST is a multiple of 4: K is a multiple of 256)
+            const int p0 = (row0 + (wave_u / S::WC) * S::WTM) / (2 * KST);  // uniform (wave_u)
+            stage(0, I0{}, false, kFoldAX && p0 == 0, F1{});
+            stage(1, I1{}, kFoldAX && p0 == 0, kFoldAX && p0 == 0, F0{});
+            for (int p = 1; p < KT / 2; ++p) {
+                stage(2 * p, I0{}, kFoldAX && p - 1 == p0, kFoldAX && p == p0, F0{});
+                stage(2 * p + 1, I1{}, kFoldAX && p == p0, kFoldAX && p == p0, F0{});
+            }
+            if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
+            mfmas(fa1, fb1);  // last sub-step of the last stage
+            wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
         };
         if constexpr (PHASE == kGram || PHASE == kPoly) {
             if (uni(int(tile.ti) - int(tile.tj)) == 0)
