@@ -3,13 +3,14 @@
 //  * k_momentum: per 128x128 tile of a Muon matrix (natural layout,
 //    padded), m <- beta*m + g, u <- g + beta*m (Nesterov) or u <- m, written
 //    as the Newton-Schulz input X0^T of the wide orientation (transposed in
-//    registers for a wide matrix), plus the tile's sum of u^2.  "Muon ... orthogonalizing momentum-smoothed matrix
-//    updates" (MatrixFSDP, arXiv 2607.05895, Abstract).
+//    registers for a wide matrix), plus the tile's sum of u^2.  Muon
+//    orthogonalises the momentum-smoothed update (MatrixFSDP, arXiv
+//    2607.05895, Abstract).
 //  * k_norm_finalize: s = 1/(||U||_F + eps) per matrix, summing the tile
 //    partials in a fixed order (bitwise deterministic, no atomics).
 //  * k_final_from_x: the parameter update straight from X0 when there are
 //    no Newton-Schulz iterations.
-//  * k_adamw: the non-matrix tail "stays on AdamW" (Abstract).
+//  * k_adamw: AdamW for the tensors that are not matrices (Abstract).
 #include <cmath>
 
 #include "device_util.h"

@@ -10,9 +10,9 @@ Source of the method: "MatrixFSDP: Communication-Free Matrix Optimizers
 Under ZeRO-3 Parameter Sharding" (arXiv 2607.05895).  Its Abstract states
 that Muon orthogonalises momentum-smoothed matrix updates with
 Newton-Schulz, that each 2D weight is handled whole on its owner, that
-non-matrix tensors stay on AdamW, and that the result must equal
-full-matrix Muon computed on the gathered matrix (Abstract; §1, the
-"gathered reference" contract).  The pages give no formulas, so every
+the remaining (non-matrix) tensors are optimised with AdamW, and that the
+result must equal full-matrix Muon computed on the gathered matrix
+(Abstract; §1).  The pages give no formulas, so every
 numeric choice below is a plain reading, listed in the design notes:
 
 * momentum: SGD-Nesterov form, m <- beta*m + g, u <- g + beta*m
@@ -80,15 +80,9 @@ class Hparams:
 
 
 # ---------------------------------------------------------------------------
-# Newton-Schulz orthogonalisation (Abstract: "orthogonalizing ... with
-# Newton-Schulz, producing spectrum-balanced updates")
+# Newton-Schulz orthogonalisation (Abstract: Muon's update is the
+# momentum-smoothed matrix made near-orthogonal by Newton-Schulz)
 # ---------------------------------------------------------------------------
-
-def quintic(sigma, a: float, b: float, c: float):
-    """The scalar polynomial p(s) = a s + b s^3 + c s^5 that one quintic
-    Newton-Schulz iteration applies to every singular value."""
-    return a * sigma + b * sigma ** 3 + c * sigma ** 5
-
 
 def newton_schulz(x: np.ndarray, steps: int, a: float, b: float, c: float) -> np.ndarray:
     """Quintic Newton-Schulz on a 2D array, returned in the input's shape.
@@ -208,8 +202,8 @@ def muon_matrix_step(w, g, m, hp: Hparams):
 
 
 # ---------------------------------------------------------------------------
-# AdamW for the non-matrix tail (Abstract: "non-matrix tensors are packed
-# into tail owners and stay on AdamW")
+# AdamW for the non-matrix tail (Abstract: tensors that are not matrices
+# are grouped onto tail owners and optimised with AdamW there)
 # ---------------------------------------------------------------------------
 
 def adamw_step(w, g, m1, m2, t: int, hp: Hparams):
