@@ -2,11 +2,12 @@
  * mfsdp.h - C ABI of the owner-local Muon + AdamW optimizer step (gfx950).
  *
  * What it computes.  "MatrixFSDP: Communication-Free Matrix Optimizers Under
- * ZeRO-3 Parameter Sharding" (arXiv 2607.05895), Abstract and §1: under
- * owner-shaped sharding one data-parallel rank holds every 2D weight whole,
- * so Muon's Newton-Schulz orthogonalisation runs locally on that owner, and
- * the non-matrix tensors packed into tail owners stay on AdamW.  The result
- * must equal full-matrix Muon on the gathered matrix (Abstract; §1).  This
+ * ZeRO-3 Parameter Sharding" (arXiv 2607.05895), Abstract and §1: with
+ * owner-shaped sharding, each 2D weight lives whole on one data-parallel
+ * rank, so that rank can run Muon's Newton-Schulz on it with no optimizer
+ * collective, while tensors that are not matrices are grouped onto tail
+ * owners and use AdamW.  The update has to be the one full-matrix Muon
+ * gives on the gathered matrix (Abstract; §1).  This
  * library is that owner-local step for one GPU: a table of whole tensors
  * (offsets, shapes, dtypes, roles; the paper's MatrixShard metadata, Abstract)
  * that live in one flat parameter buffer, and one call that updates all of
@@ -101,6 +102,18 @@ typedef struct mfsdp_hparams {
                                  ZeRO-3-scale memory the MatrixFSDP abstract asks for), and the
                                  momentum pass then moves 8 B per bf16 element instead of 12.  The
                                  AdamW moments stay fp32. */
+    int32_t ns_tile_gram;     /* output tile edge of the Newton-Schulz Gram contraction: 0 = chosen by
+                                 the planner (256 when the phase has at least 512 tiles of 256, else
+                                 128), or 128 or 256 to force it (for tests and tuning; the result
+                                 is the same up to fp32 summation order) */
+    int32_t ns_tile_poly;     /* the same for the polynomial B = b A + c A A */
+    int32_t ns_tile_update;   /* the same for the update X <- a X + B X; a forced edge also turns off
+                                 the planner's split of a short last round of 256-tiles into 128-tiles */
+    uint32_t guard_bytes;     /* 0 normally.  Otherwise at most 16 MiB: the plan leaves this many
+                                 bytes (rounded up to 256) unused after every region it lays out in
+                                 the state and in the workspace (mfsdp_plan_regions lists them), so
+                                 that a test can fill the gaps with canaries and check after a step
+                                 that no kernel wrote outside its regions.  Costs only memory. */
 } mfsdp_hparams;
 
 typedef struct mfsdp_plan_s* mfsdp_plan_t;
@@ -115,6 +128,18 @@ typedef struct mfsdp_entry_info {
     uint64_t ns_out_offset;   /* Muon: element offset of the fp32 O export in ns_out */
     float lr_scale;           /* Muon: the shape scale applied to lr */
 } mfsdp_entry_info;
+
+/* Which caller buffer a plan region lies in. */
+#define MFSDP_BUFFER_STATE 0
+#define MFSDP_BUFFER_WORKSPACE 1
+
+/* One region the plan lays out in the state or the workspace. */
+typedef struct mfsdp_region {
+    uint64_t offset;          /* bytes into the buffer */
+    uint64_t bytes;           /* bytes the step may read or write there */
+    int32_t buffer;           /* MFSDP_BUFFER_STATE or MFSDP_BUFFER_WORKSPACE */
+    int32_t entry;            /* table entry it belongs to, -1 for a region shared by all entries */
+} mfsdp_region;
 
 /* Step flags. */
 #define MFSDP_STEP_DESCRIPTORS_RESIDENT 1u  /* the workspace already holds this plan's
@@ -147,14 +172,10 @@ typedef struct mfsdp_step_args {
  * buffer, used for bounds checks.  hp: copied into the plan.
  * Errors: INVALID_ARGUMENT (null pointer, n < 0, negative dim, entry past
  * param_bytes, bad hyper-parameter), OVERLAP, MISALIGNED, UNSUPPORTED (dtype,
- * role, ns_precision, momentum_dtype, a dimension above 2^22, a Muon matrix
- * whose padded Newton-Schulz buffer reaches 2 GiB).  *out is set only on
- * success.
- * The environment variable MFSDP_TILE, read here, overrides the output tile
- * edge of the Newton-Schulz contractions (for tests and tuning): "E" for
- * every phase or "G,P,U" for the Gram, polynomial and update phases, each
- * 128 or 256; other values are ignored.  By default a phase uses 256 when it
- * has at least 512 tiles of that edge, else 128. */
+ * role, ns_precision, momentum_dtype, an ns_tile_* other than 0, 128 and
+ * 256, a dimension above 2^22, a Muon matrix whose padded Newton-Schulz
+ * buffer reaches 2 GiB).  *out is set only on success.  The plan depends on
+ * its arguments only (no environment variable is read). */
 mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n, uint64_t param_bytes,
                                const mfsdp_hparams* hp, mfsdp_plan_t* out);
 
@@ -186,6 +207,18 @@ mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsdp_entry_inf
  * table, step < 1 with an AdamW entry, misaligned workspace, too few
  * events), WORKSPACE_TOO_SMALL, HIP. */
 mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args);
+
+/* Every region the plan lays out, state first, then workspace, each in
+ * increasing offset: Muon momentum and AdamW first and second moments in the
+ * state; in the workspace the descriptor blob (one region: it is uploaded
+ * as one copy), the per-matrix scale factors, the norm partial sums, and per
+ * Muon matrix its two X^T buffers and its A and B.  The step reads and
+ * writes state and workspace bytes inside these regions only.  Writes
+ * min(*count, capacity) entries to regions (which may be NULL when capacity
+ * is 0) and the total number to *count.  Host only.
+ * Errors: INVALID_ARGUMENT (NULL plan or count, capacity < 0, NULL regions
+ * with capacity > 0). */
+mfsdp_status mfsdp_plan_regions(mfsdp_plan_t plan, mfsdp_region* regions, int64_t capacity, int64_t* count);
 
 /* Free a plan.  NULL is accepted. */
 mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
@@ -285,7 +318,15 @@ mfsdp_status mfsdp_owner_scatter(mfsdp_plan_t plan, const void* const* tensors, 
                                  const void* const* state2, void* params, uint64_t param_bytes, void* state,
                                  uint64_t state_bytes);
 
-/* Static description of a status code. */
+/* ---- Measurement probes (NOT part of the optimizer step) ----
+ *
+ * The two calls below compute nothing of the owner step and touch none of
+ * a plan's buffers.  They exist so that a benchmark can report, on the
+ * same GPU and in the same run, the rates the part sustains for the two
+ * kinds of work the step does (bf16 MFMA on Gaussian data; HBM streaming),
+ * beside the published peaks.  A caller that only runs the optimizer never
+ * needs them. */
+
 /* Measurement support (not part of the step): enqueue on `stream` a
  * register-only loop of bf16 MFMAs (v_mfma_f32_32x32x16_bf16, fp32
  * accumulate) over `blocks` blocks of 4 waves, each wave running `iters`
@@ -311,6 +352,7 @@ mfsdp_status mfsdp_probe_mfma_bf16(const void* operands, uint64_t operand_bytes,
  * not a nonzero multiple of 16, misaligned buffer), HIP. */
 mfsdp_status mfsdp_probe_hbm(void* dst, const void* src, uint64_t bytes, int32_t mode, float* sink, void* stream);
 
+/* Static description of a status code. */
 const char* mfsdp_status_string(mfsdp_status status);
 
 /* Thread-local description of the last error on this thread ("" if none). */

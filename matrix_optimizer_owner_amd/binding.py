@@ -47,6 +47,8 @@ class Hparams(ctypes.Structure):
         ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
         ("adam_eps", ctypes.c_float), ("adam_weight_decay", ctypes.c_float),
         ("momentum_dtype", ctypes.c_int32),
+        ("ns_tile_gram", ctypes.c_int32), ("ns_tile_poly", ctypes.c_int32), ("ns_tile_update", ctypes.c_int32),
+        ("guard_bytes", ctypes.c_uint32),
     ]
 
 
@@ -54,6 +56,14 @@ class EntryInfo(ctypes.Structure):
     _fields_ = [("role", ctypes.c_int32), ("transposed", ctypes.c_int32), ("m", ctypes.c_int64),
                 ("n", ctypes.c_int64), ("state_offset", ctypes.c_uint64), ("state_offset2", ctypes.c_uint64),
                 ("ns_out_offset", ctypes.c_uint64), ("lr_scale", ctypes.c_float)]
+
+
+BUFFER_STATE, BUFFER_WORKSPACE = 0, 1
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("bytes", ctypes.c_uint64), ("buffer", ctypes.c_int32),
+                ("entry", ctypes.c_int32)]
 
 
 class StepArgs(ctypes.Structure):
@@ -80,7 +90,8 @@ class TensorPlace(ctypes.Structure):
 
 EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
-    "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_owner_step", "mfsdp_plan_destroy",
+    "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_plan_regions",
+    "mfsdp_owner_step", "mfsdp_plan_destroy",
     "mfsdp_owner_partition", "mfsdp_owner_gather", "mfsdp_owner_scatter", "mfsdp_status_string",
     "mfsdp_last_error_message", "mfsdp_probe_mfma_bf16", "mfsdp_probe_hbm",
 )
@@ -106,6 +117,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_plan_num_events.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     lib.mfsdp_plan_num_entries.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.mfsdp_plan_entry_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(EntryInfo)]
+    lib.mfsdp_plan_regions.argtypes = [P, ctypes.POINTER(Region), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
     lib.mfsdp_owner_step.argtypes = [P, ctypes.POINTER(StepArgs)]
     lib.mfsdp_plan_destroy.argtypes = [P]
     lib.mfsdp_owner_partition.argtypes = [ctypes.POINTER(Tensor), ctypes.c_int64, ctypes.POINTER(PartitionParams),
@@ -141,15 +153,24 @@ def _check(status: int) -> None:
 
 
 def make_hparams(**kw) -> Hparams:
-    """Hyper-parameters with Muon/AdamW defaults; keyword overrides."""
+    """Hyper-parameters with Muon/AdamW defaults; keyword overrides.
+    ``ns_tile=E`` or ``ns_tile=(G, P, U)`` is shorthand for the three
+    ns_tile_* fields (the output tile edge of the Gram, polynomial and update
+    contractions: 0 = the planner's choice, 128 or 256)."""
+    if "ns_tile" in kw:
+        t = kw.pop("ns_tile")
+        g, p, u = (t, t, t) if isinstance(t, int) else tuple(t)
+        kw.update(ns_tile_gram=g, ns_tile_poly=p, ns_tile_update=u)
     d = dict(lr=0.02, weight_decay=0.01, momentum=0.95, nesterov=1, ns_steps=5, ns_a=3.4445, ns_b=-4.7750,
              ns_c=2.0315, ns_eps=1e-7, lr_scale_mode=0, ns_precision=0, adam_lr=0.02, adam_beta1=0.9,
-             adam_beta2=0.95, adam_eps=1e-8, adam_weight_decay=0.01, momentum_dtype=0)
+             adam_beta2=0.95, adam_eps=1e-8, adam_weight_decay=0.01, momentum_dtype=0, ns_tile_gram=0,
+             ns_tile_poly=0, ns_tile_update=0, guard_bytes=0)
     unknown = set(kw) - set(d)
     if unknown:
         raise KeyError(f"unknown hyper-parameters {sorted(unknown)}")
     d.update(kw)
-    ints = {"nesterov", "ns_steps", "lr_scale_mode", "ns_precision", "momentum_dtype"}
+    ints = {"nesterov", "ns_steps", "lr_scale_mode", "ns_precision", "momentum_dtype", "ns_tile_gram",
+            "ns_tile_poly", "ns_tile_update", "guard_bytes"}
     return Hparams(**{k: (int(v) if k in ints else float(v)) for k, v in d.items()})
 
 
@@ -203,6 +224,14 @@ class OwnerPlan:
         info = EntryInfo()
         _check(self._lib.mfsdp_plan_entry_info(self._h, i, ctypes.byref(info)))
         return info
+
+    def regions(self) -> list:
+        """Every state and workspace region of the plan (mfsdp_plan_regions)."""
+        n = ctypes.c_int64()
+        _check(self._lib.mfsdp_plan_regions(self._h, None, 0, ctypes.byref(n)))
+        arr = (Region * max(1, n.value))()
+        _check(self._lib.mfsdp_plan_regions(self._h, arr, n.value, ctypes.byref(n)))
+        return [arr[k] for k in range(n.value)]
 
     def num_events(self) -> int:
         v = ctypes.c_uint32()

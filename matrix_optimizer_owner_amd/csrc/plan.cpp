@@ -9,8 +9,6 @@
 // non-owners hold empty shards).
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
-#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -43,12 +41,16 @@ mfsdp_status check_hparams(const mfsdp_hparams& hp) {
     if (hp.ns_steps < 0 || hp.ns_steps > 64)
         return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_steps must be in [0, 64]");
     if (hp.ns_eps < 0.f) return fail(MFSDP_ERR_INVALID_ARGUMENT, "ns_eps must be >= 0");
+    if (hp.guard_bytes > (1u << 24)) return fail(MFSDP_ERR_INVALID_ARGUMENT, "guard_bytes above 16 MiB");
     if (hp.momentum_dtype != MFSDP_F32 && hp.momentum_dtype != MFSDP_BF16)
         return fail(MFSDP_ERR_UNSUPPORTED, "momentum_dtype must be MFSDP_F32 or MFSDP_BF16");
     if (hp.lr_scale_mode != 0 && hp.lr_scale_mode != 1)
         return fail(MFSDP_ERR_UNSUPPORTED, "lr_scale_mode must be 0 or 1");
     if (hp.ns_precision != 0 && hp.ns_precision != 1)
         return fail(MFSDP_ERR_UNSUPPORTED, "ns_precision must be 0 (bf16) or 1 (fp32)");
+    for (int t : {hp.ns_tile_gram, hp.ns_tile_poly, hp.ns_tile_update})
+        if (t != 0 && t != kTileSmall && t != kTileLarge)
+            return fail(MFSDP_ERR_UNSUPPORTED, "ns_tile_* must be 0 (planner's choice), 128 or 256");
     if (hp.nesterov != 0 && hp.nesterov != 1)
         return fail(MFSDP_ERR_INVALID_ARGUMENT, "nesterov must be 0 or 1");
     if (hp.adam_beta1 < 0.f || hp.adam_beta1 >= 1.f || hp.adam_beta2 < 0.f || hp.adam_beta2 >= 1.f)
@@ -176,23 +178,29 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             }
 
         // ---- state layout: Muon momentum (momentum_dtype), then AdamW moments (fp32) ----
+        // every region is followed by `guard` unused bytes (0 unless the
+        // caller asked for guard bands)
+        const uint64_t guard = align_up(uint64_t(hp->guard_bytes), kAlign);
         const uint64_t mom_bytes = hp->momentum_dtype == MFSDP_BF16 ? 2 : 4;
         uint64_t soff = 0;
+        auto state_region = [&](uint64_t bytes, int64_t entry) {
+            const uint64_t at = soff;
+            plan->regions.push_back(mfsdp_region{at, bytes, MFSDP_BUFFER_STATE, int32_t(entry)});
+            soff = align_up(soff + bytes, kAlign) + guard;
+            return at;
+        };
         for (int64_t i = 0; i < n; ++i) {
             mfsdp_entry_info& inf = plan->info[size_t(i)];
             if (inf.role != MFSDP_ROLE_MUON) continue;
             const uint64_t numel = uint64_t(entries[i].rows) * uint64_t(entries[i].cols);
-            inf.state_offset = soff;
-            soff = align_up(soff + numel * mom_bytes, kAlign);
+            inf.state_offset = state_region(numel * mom_bytes, i);
         }
         for (int64_t i = 0; i < n; ++i) {
             mfsdp_entry_info& inf = plan->info[size_t(i)];
             if (inf.role != MFSDP_ROLE_ADAMW) continue;
             const uint64_t numel = uint64_t(entries[i].rows) * uint64_t(entries[i].cols);
-            inf.state_offset = soff;
-            soff = align_up(soff + numel * 4, kAlign);
-            inf.state_offset2 = soff;
-            soff = align_up(soff + numel * 4, kAlign);
+            inf.state_offset = state_region(numel * 4, i);
+            inf.state_offset2 = state_region(numel * 4, i);
         }
         plan->state_bytes = soff;
 
@@ -273,16 +281,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             }
             return c;
         };
-        // tuning override MFSDP_TILE: "E" for every phase or "G,P,U" per phase (E, G, P, U in {128, 256})
-        int forced[3] = {0, 0, 0};
-        if (const char* f = std::getenv("MFSDP_TILE")) {
-            int v[3] = {0, 0, 0};
-            const int got = std::sscanf(f, "%d,%d,%d", &v[0], &v[1], &v[2]);
-            for (int k = 0; k < 3; ++k) {
-                const int x = got == 3 ? v[k] : v[0];
-                if (x == kTileSmall || x == kTileLarge) forced[k] = x;
-            }
-        }
+        // tile edges forced by the caller (0: the planner's choice)
+        const int forced[3] = {hp->ns_tile_gram, hp->ns_tile_poly, hp->ns_tile_update};
         auto pick = [&](int phase, bool upper, bool full_n) {
             if (forced[phase]) return forced[phase];
             return count(upper, full_n, kTileLarge) >= kLargeTileMin ? kTileLarge : kTileSmall;
@@ -339,6 +339,13 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             off = align_up(off + bytes, kAlign);
             return at;
         };
+        // a region of its own, followed by the guard gap
+        auto region = [&](uint64_t bytes, int64_t entry) {
+            const uint64_t at = off;
+            plan->regions.push_back(mfsdp_region{at, bytes, MFSDP_BUFFER_WORKSPACE, int32_t(entry)});
+            off = align_up(off + bytes, kAlign) + guard;
+            return at;
+        };
         w.off_mat = section(mats.size() * sizeof(MatDesc));
         w.off_k1_begin = section(k1_begin.size() * sizeof(int32_t));
         w.off_gram = section(gram.size() * sizeof(Tile));
@@ -348,16 +355,19 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
         w.off_tail = section(tails.size() * sizeof(TailDesc));
         w.off_tail_begin = section(tail_begin.size() * sizeof(int32_t));
         w.desc_bytes = off;
-        w.off_s = section(mats.size() * sizeof(float));
-        w.off_partials = section(uint64_t(k1_begin.back()) * sizeof(float));
+        // the descriptor blob is uploaded by one copy, so it is one region
+        plan->regions.push_back(mfsdp_region{0, off, MFSDP_BUFFER_WORKSPACE, -1});
+        off += guard;
+        w.off_s = region(mats.size() * sizeof(float), -1);
+        w.off_partials = region(uint64_t(k1_begin.back()) * sizeof(float), -1);
         for (size_t k = 0; k < mats.size(); ++k) {
             MatDesc& d = mats[k];
             const uint64_t xbytes = uint64_t(d.ld) * uint64_t(d.np) * uint64_t(es);
             const uint64_t abytes = uint64_t(d.ld) * uint64_t(d.mp) * uint64_t(es);
-            d.x_off[0] = section(xbytes);
-            d.x_off[1] = section(xbytes);
-            d.a_off = section(abytes);
-            d.b_off = section(abytes);
+            d.x_off[0] = region(xbytes, mat_entry[k]);
+            d.x_off[1] = region(xbytes, mat_entry[k]);
+            d.a_off = region(abytes, mat_entry[k]);
+            d.b_off = region(abytes, mat_entry[k]);
         }
         w.total_bytes = off;
         w.n_mat = nm;
@@ -435,6 +445,17 @@ extern "C" mfsdp_status mfsdp_plan_entry_info(mfsdp_plan_t plan, int64_t i, mfsd
     if (!plan || !info) return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL argument");
     if (i < 0 || i >= int64_t(plan->entries.size())) return fail(MFSDP_ERR_INVALID_ARGUMENT, "entry index out of range");
     *info = plan->info[size_t(i)];
+    return MFSDP_OK;
+}
+
+extern "C" mfsdp_status mfsdp_plan_regions(mfsdp_plan_t plan, mfsdp_region* regions, int64_t capacity,
+                                           int64_t* count) {
+    clear_error();
+    if (!plan || !count) return fail(MFSDP_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (capacity < 0 || (capacity > 0 && !regions)) return fail(MFSDP_ERR_INVALID_ARGUMENT, "bad capacity or NULL regions");
+    const int64_t n = int64_t(plan->regions.size());
+    *count = n;
+    for (int64_t k = 0; k < std::min(n, capacity); ++k) regions[k] = plan->regions[size_t(k)];
     return MFSDP_OK;
 }
 

@@ -13,6 +13,7 @@ struct mfsdp_plan_s {
     mfsdp_hparams hp;
     mfsdp::WorkspaceMap map;
     std::vector<uint8_t> desc_blob;   // copied to the start of the workspace
+    std::vector<mfsdp_region> regions;  // every state and workspace region, in layout order
     uint64_t state_bytes = 0;
     uint64_t ns_out_elems = 0;
     uint64_t max_param_end = 0;       // highest byte any entry touches

@@ -17,7 +17,10 @@ int main(void) {
     OF(mfsdp_hparams, ns_steps); OF(mfsdp_hparams, ns_a); OF(mfsdp_hparams, ns_b); OF(mfsdp_hparams, ns_c);
     OF(mfsdp_hparams, ns_eps); OF(mfsdp_hparams, lr_scale_mode); OF(mfsdp_hparams, ns_precision);
     OF(mfsdp_hparams, adam_lr); OF(mfsdp_hparams, adam_beta1); OF(mfsdp_hparams, adam_beta2); OF(mfsdp_hparams, adam_eps);
-    OF(mfsdp_hparams, adam_weight_decay); OF(mfsdp_hparams, momentum_dtype);
+    OF(mfsdp_hparams, adam_weight_decay); OF(mfsdp_hparams, momentum_dtype); OF(mfsdp_hparams, ns_tile_gram);
+    OF(mfsdp_hparams, ns_tile_poly); OF(mfsdp_hparams, ns_tile_update); OF(mfsdp_hparams, guard_bytes);
+    SZ(mfsdp_region);
+    OF(mfsdp_region, offset); OF(mfsdp_region, bytes); OF(mfsdp_region, buffer); OF(mfsdp_region, entry);
     SZ(mfsdp_entry_info);
     OF(mfsdp_entry_info, role); OF(mfsdp_entry_info, transposed); OF(mfsdp_entry_info, m); OF(mfsdp_entry_info, n);
     OF(mfsdp_entry_info, state_offset); OF(mfsdp_entry_info, state_offset2); OF(mfsdp_entry_info, ns_out_offset);

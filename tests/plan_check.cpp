@@ -2,11 +2,14 @@
 // with g++ against plan.cpp; no HIP).  Reads a table from stdin:
 //   ns_precision n
 //   offset rows cols dtype role      (n lines)
-// and checks the descriptor blob and layout invariants.  Prints "OK <stats>"
-// or the first violation, and returns non-zero on a violation.
+// and checks the descriptor blob and layout invariants.  Optional arguments
+// G P U force the tile edges of the Gram, polynomial and update (the plan's
+// ns_tile_* options; 0 = the planner's choice).  Prints "OK <stats>" or the
+// first violation, and returns non-zero on a violation.
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <set>
 #include <tuple>
@@ -27,7 +30,7 @@ static int fail_count = 0;
         }                                         \
     } while (0)
 
-int main() {
+int main(int argc, char** argv) {
     int prec = 0;
     long long n = 0;
     if (std::scanf("%d %lld", &prec, &n) != 2) return 2;
@@ -50,6 +53,11 @@ int main() {
     hp.lr = 0.02f; hp.weight_decay = 0.01f; hp.momentum = 0.95f; hp.nesterov = 1; hp.ns_steps = 5;
     hp.ns_a = 3.4445f; hp.ns_b = -4.775f; hp.ns_c = 2.0315f; hp.ns_eps = 1e-7f; hp.ns_precision = prec;
     hp.adam_lr = 0.02f; hp.adam_beta1 = 0.9f; hp.adam_beta2 = 0.95f; hp.adam_eps = 1e-8f; hp.adam_weight_decay = 0.01f;
+    if (argc >= 4) {
+        hp.ns_tile_gram = std::atoi(argv[1]);
+        hp.ns_tile_poly = std::atoi(argv[2]);
+        hp.ns_tile_update = std::atoi(argv[3]);
+    }
     mfsdp_plan_t plan = nullptr;
     const mfsdp_status st = mfsdp_plan_create(es.data(), n, pbytes, &hp, &plan);
     CHECK(st == MFSDP_OK, "plan_create failed: %s", mfsdp_last_error_message());

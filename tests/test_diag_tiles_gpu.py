@@ -28,10 +28,9 @@ def diag_table(precision: int) -> W.Workload:
 
 
 @pytest.mark.parametrize("tile", ["256", "128"])
-def test_diagonal_tiles_bf16(tile, monkeypatch):
-    monkeypatch.setenv("MFSDP_TILE", tile)
+def test_diagonal_tiles_bf16(tile):
     wl = diag_table(0)
-    run = DeviceRun(wl)
+    run = DeviceRun(wl, {"ns_tile": int(tile)})
     for t in (1, 2):
         say(f"[diag-tiles tile={tile}] step {t}: {wl.name}")
         run.fill(t, params_too=(t == 1))

@@ -49,6 +49,7 @@ def test_struct_layouts_match_header(tmp_path):
     out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     mirrors = {"mfsdp_entry": B.Entry, "mfsdp_hparams": B.Hparams, "mfsdp_entry_info": B.EntryInfo,
                "mfsdp_step_args": B.StepArgs, "mfsdp_tensor": B.Tensor, "mfsdp_partition_params": B.PartitionParams,
+               "mfsdp_region": B.Region,
                "mfsdp_tensor_place": B.TensorPlace}
     checked = 0
     for line in filter(None, out):
@@ -206,17 +207,33 @@ def test_update_wave_tail_split(plan_checker):
     assert "upd=1280+64 " in out, out
     out = subprocess.run([plan_checker], input=_table_text(W.config(2)), capture_output=True, text=True).stdout
     assert "upd=13312+0 " in out, out
-    out = subprocess.run([plan_checker], input=_table_text(W.config(1)), capture_output=True, text=True,
-                         env=dict(os.environ, MFSDP_TILE="256")).stdout
+    out = subprocess.run([plan_checker, "256", "256", "256"], input=_table_text(W.config(1)), capture_output=True,
+                         text=True).stdout
     assert "upd=1296+0 " in out, out
 
 
 def test_tile_override_keeps_invariants(plan_checker):
+    """The plan's ns_tile_* options force the tile edges; every invariant
+    still holds, and the environment plays no part in the plan."""
     wl = W.config(1)
-    for t in ("128", "256", "256,128,256"):
-        res = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True,
-                             env=dict(os.environ, MFSDP_TILE=t))
+    for t in (("128",) * 3, ("256",) * 3, ("256", "128", "256"), ("0", "256", "0")):
+        res = subprocess.run([plan_checker, *t], input=_table_text(wl), capture_output=True, text=True)
         assert res.returncode == 0, res.stdout
+        assert res.stdout.startswith("OK"), res.stdout
+    base = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True).stdout
+    env = subprocess.run([plan_checker], input=_table_text(wl), capture_output=True, text=True,
+                         env=dict(os.environ, MFSDP_TILE="256")).stdout
+    assert env == base
+
+
+def test_tile_option_validation():
+    """ns_tile_* accept 0, 128 and 256 only."""
+    for bad in (64, 512, -1, 1):
+        with pytest.raises(B.MfsdpError) as ei:
+            _plan([B.TableEntry(0, 64, 64)], ns_tile_poly=bad)
+        assert ei.value.status == 4
+    p = _plan([B.TableEntry(0, 64, 64)], ns_tile=(128, 256, 0))
+    assert p.workspace_bytes > 0
 
 
 def test_step_argument_checks_without_gpu():
@@ -277,3 +294,43 @@ def test_hbm_probe_argument_checks_without_gpu(lib):
     assert lib.mfsdp_probe_hbm(None, p, 64, 1, s, None) == 1   # write without dst
     assert lib.mfsdp_probe_hbm(p, p, 60, 2, s, None) == 1      # not a multiple of 16
     assert lib.mfsdp_probe_hbm(p, p, 64, 2, None, None) == 1   # no sink
+
+
+@pytest.mark.parametrize("guard", [0, 1000, 4096])
+def test_regions_partition_state_and_workspace(guard):
+    """mfsdp_plan_regions lists, per buffer, disjoint regions in increasing
+    order inside the buffer: one momentum region per Muon entry and two
+    moment regions per AdamW entry (at entry_info's offsets), the descriptor
+    blob, the scale factors, the norm partials and four Newton-Schulz
+    buffers per Muon matrix; with guard_bytes every region is followed by at
+    least that many unused bytes (rounded up to 256), and without it the
+    layout is the one the plan has always had."""
+    wl = W.small_ragged()
+    offs, pbytes = wl.layout()
+    ents = [B.TableEntry(o, s.rows, s.cols, B.BF16 if s.dtype == "bf16" else B.F32) for o, s in zip(offs, wl.specs)]
+    p = B.OwnerPlan(ents, pbytes, B.make_hparams(guard_bytes=guard))
+    p0 = B.OwnerPlan(ents, pbytes, B.make_hparams())
+    regs = p.regions()
+    g = (guard + 255) // 256 * 256
+    for buf, size in ((B.BUFFER_STATE, p.state_bytes), (B.BUFFER_WORKSPACE, p.workspace_bytes)):
+        rs = [r for r in regs if r.buffer == buf]
+        for a, b in zip(rs, rs[1:]):
+            assert a.offset + a.bytes + g <= b.offset, (a.offset, a.bytes, b.offset)
+        assert rs[-1].offset + rs[-1].bytes + g <= size
+    infos = [p.entry_info(i) for i in range(len(ents))]
+    st = {(r.entry, r.offset) for r in regs if r.buffer == B.BUFFER_STATE}
+    ws = [r for r in regs if r.buffer == B.BUFFER_WORKSPACE]
+    for i, inf in enumerate(infos):
+        s = wl.specs[i]
+        if inf.role == B.ROLE_MUON:
+            assert (i, inf.state_offset) in st
+            assert sum(1 for r in ws if r.entry == i) == 4
+        elif inf.role == B.ROLE_ADAMW:
+            assert (i, inf.state_offset) in st and (i, inf.state_offset2) in st
+    assert sum(1 for r in ws if r.entry == -1) == 3
+    if guard == 0:
+        assert p.workspace_bytes == p0.workspace_bytes and p.state_bytes == p0.state_bytes
+        assert [(x.state_offset, x.state_offset2) for x in infos] == \
+            [(x.state_offset, x.state_offset2) for x in (p0.entry_info(i) for i in range(len(ents)))]
+    else:
+        assert p.workspace_bytes > p0.workspace_bytes and p.state_bytes > p0.state_bytes

@@ -52,11 +52,9 @@ def random_table(seed: int, precision: int) -> W.Workload:
 
 @pytest.mark.parametrize("seed,precision,tile", [(21, 0, None), (22, 0, "256"), (23, 1, None), (24, 0, "256"),
                                                  (25, 0, "256"), (26, 1, "256"), (27, 0, "128")])
-def test_random_tables(seed, precision, tile, monkeypatch):
-    if tile:
-        monkeypatch.setenv("MFSDP_TILE", tile)
+def test_random_tables(seed, precision, tile):
     wl = random_table(seed, precision)
-    run = DeviceRun(wl)
+    run = DeviceRun(wl, {"ns_tile": int(tile)} if tile else None)
     try:
         for t in (1, 2):
             say(f"[random s{seed} p{precision} tile={tile}] step {t}: {[(s.rows, s.cols) for s in wl.specs]}")
