@@ -868,27 +868,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         // a X folded into the accumulators (update phases): X^T[n][k] sits in
         // Q's stage slot, so in the sub-steps whose contraction indices k0 ..
         // k0+15 fall in this wave's output rows m, the MFMA of an identity
-        // fragment with Q's fragments adds a * X[m][n] for those rows, a split
-        // as ahi + alo in bf16 (two MFMAs, products exact in fp32).  Lane
-        // (frow, fhalf) of an identity fragment holds contraction indices
-        // 8*fhalf .. 8*fhalf+7 of row frow: one nonzero when the sub-step
-        // starts ro = 16*RO rows into the 32-row MFMA block BLK.  The
-        // fragments are rebuilt at each use (a few VALU operations) rather
-        // than held in 16 registers across the loop.
+        // fragment with Q's fragments adds a * X[m][n] for those rows.  The
+        // fp32 coefficient a is split exactly into three bf16 terms, a = ahi +
+        // amid + alo (each RNE of what the previous terms leave: ahi holds the
+        // top 8 significant bits, a - ahi has at most 16, a - ahi - amid at
+        // most 8), so every identity product is exact in fp32 and a X enters
+        // the accumulator as three fp32 additions.  Lane (frow, fhalf) of an
+        // identity fragment holds contraction indices 8*fhalf .. 8*fhalf+7 of
+        // row frow: one nonzero when the sub-step starts ro = 16*RO rows into
+        // the 32-row MFMA block BLK.  The fragments are rebuilt at each use (a
+        // few VALU operations) rather than held in registers across the loop.
         const uint16_t ahi = f32_to_bf16(a.ca);
-        const uint16_t alo = f32_to_bf16(a.ca - bf16_to_f32(ahi));
+        const float ar1 = a.ca - bf16_to_f32(ahi);
+        const uint16_t amid = f32_to_bf16(ar1);
+        const uint16_t alo = f32_to_bf16(ar1 - bf16_to_f32(amid));
         auto fold = [&](auto blk, auto ro, const u32x4_t (&fb)[MN]) {
             int t = frow - 16 * decltype(ro)::value - 8 * fhalf;
             asm volatile("" : "+v"(t));  // keeps the fragments out of loop-invariant hoisting
-            u32x4_t ih, il;
+            u32x4_t ih, im, il;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const bool on = t >= 0 && t < 8 && (t >> 1) == w;
                 ih[w] = on ? uint32_t(ahi) << (16 * (t & 1)) : 0u;
+                im[w] = on ? uint32_t(amid) << (16 * (t & 1)) : 0u;
                 il[w] = on ? uint32_t(alo) << (16 * (t & 1)) : 0u;
             }
 #pragma unroll
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], ih, fb[jj]);
+#pragma unroll
+            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], im, fb[jj]);
 #pragma unroll
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], il, fb[jj]);
             __builtin_amdgcn_sched_barrier(0);

@@ -97,23 +97,21 @@ def test_bf16_momentum_gpt2():
 
 
 @pytest.mark.parametrize("precision", [0, 1])
-def test_ragged_shapes_on_256_tiles(precision, monkeypatch):
+def test_ragged_shapes_on_256_tiles(precision):
     """Force the 256x256 tile kernels (for bf16: the locked 4-wave schedule
     with the folded a X in the update phases) onto shapes that are not multiples of
     256, so their padding and the final update's bounds are exercised."""
-    monkeypatch.setenv("MFSDP_TILE", "256")
-    _steps(W.small_ragged(precision=precision), 2, label=f"t256-p{precision}")
+    _steps(W.small_ragged(precision=precision), 2, {"ns_tile": 256}, label=f"t256-p{precision}")
 
 
 @pytest.mark.parametrize("coeffs", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
-def test_other_coefficients_on_256_tiles(coeffs, monkeypatch):
+def test_other_coefficients_on_256_tiles(coeffs):
     """Other iteration coefficients on the 256-tile bf16 kernels (the cubic
     iteration, c = 0, and a second quintic): the folded a X and the
     polynomial's b A + c A^2 epilogue take the coefficients from the
     parameters, and the oracle runs the same coefficients."""
-    monkeypatch.setenv("MFSDP_TILE", "256")
     a, b, c = coeffs
-    _steps(W.small_ragged(precision=0), 1, {"ns_a": a, "ns_b": b, "ns_c": c}, label=f"coef{a},{b},{c}")
+    _steps(W.small_ragged(precision=0), 1, {"ns_a": a, "ns_b": b, "ns_c": c, "ns_tile": 256}, label=f"coef{a},{b},{c}")
 
 
 def test_bitwise_deterministic():
@@ -136,5 +134,39 @@ def test_bitwise_deterministic():
             same = bool(run.torch.equal(x.view(run.torch.uint8), y.view(run.torch.uint8)))
             say(f"  {name}: bitwise equal = {same}")
             assert same, name
+    finally:
+        run.free()
+
+
+@pytest.mark.parametrize("tile", [256, 128])
+def test_ax_term_exact(tile):
+    """With b = c = 0 and one iteration, O = a X exactly: X0 = G (bf16
+    gradients, zero momentum, plain momentum, so u = G and its bf16 cast is
+    exact) and B = 0, so the update is the a X term alone, scaled by s.  On
+    256-tiles a X enters through identity-fragment MFMAs with a split into
+    three bf16 terms; on 128-tiles the epilogue adds a X in fp32.  Either
+    way O must equal a G / (||G||_F + eps) of the oracle to fp32 rounding
+    (1e-6 relative, per matrix, in Frobenius and elementwise against
+    max |O|); a two-term split of a = 3.4445 would leave 3.3e-6."""
+    from oracle import muon_oracle as orc
+    from tests.harness import oracle_hparams
+
+    sp = [W.TensorSpec("sq", 256, 256, grad_std=1e-2), W.TensorSpec("wide", 512, 1024, grad_std=1e-3),
+          W.TensorSpec("ragged", 300, 700, grad_std=1e-1), W.TensorSpec("tall", 1100, 260, grad_std=1e-3)]
+    wl = W.Workload("ax-exact", sp, seed=41, hparams=dict(W.MUON_DEFAULTS, ns_precision=0))
+    run = DeviceRun(wl, {"ns_tile": tile, "nesterov": 0, "ns_steps": 1, "ns_a": 3.4445, "ns_b": 0.0, "ns_c": 0.0})
+    hp = oracle_hparams(run.hp)
+    try:
+        run.fill(1, params_too=True)
+        snap = run.snapshot_entries(range(len(sp)))
+        run.run(1)
+        for i, s in enumerate(sp):
+            _, u = orc.momentum_step(snap[(i, "state")], snap[(i, "grad")], hp)
+            o_orc = orc.newton_schulz(orc.frobenius_normalise(u, hp.ns_eps), 1, hp.ns_a, hp.ns_b, hp.ns_c)
+            o = run.dev_entry(i, "o")
+            rel = np.linalg.norm(o - o_orc) / np.linalg.norm(o_orc)
+            mx = np.max(np.abs(o - o_orc)) / np.max(np.abs(o_orc))
+            say(f"  [ax-exact tile={tile}] {s.name} {s.rows}x{s.cols}: rel={rel:.3e} max/max={mx:.3e}")
+            assert rel <= 1e-6 and mx <= 1e-6, (s.name, rel, mx)
     finally:
         run.free()
