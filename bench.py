@@ -9,10 +9,15 @@ synthetic and resident in HBM before the timed region.  Prints ONE JSON line.
     python bench.py [--steps K] [--warmup W] [--config I] [--gpus 1]
 
 --config selects the workload (0 single 256x512 fp32, 1 GPT-2-small owner
-buffer, 2 Llama-3-8B owner share (default), 3 mixed 256-matrix stress,
-4 Llama-3-70B owner share, 5 a tail-only buffer of 268 M fp32 elements that
-measures the AdamW kernel against HBM bandwidth).  --copy-probe-gib G instead runs a plain device
-copy of G GiB (used to scale the HBM byte counters of rocprofv3).
+buffer, 2 Llama-3-8B owner share, 3 mixed 256-matrix stress (default: the
+largest workload in Newton-Schulz FLOPs), 4 Llama-3-70B owner share, 5 a
+tail-only buffer of 268 M fp32 elements that measures the AdamW kernel
+against HBM bandwidth).  --copy-probe-gib G instead runs a plain device copy
+of G GiB (used to scale the HBM byte counters of rocprofv3).
+
+Every step, warm-up included, reads its own seeded gradient: up to --steps
+gradient buffers (at most --grad-pool-gb of them) are generated before the
+timed region, and step k reads buffer k modulo their number.
 """
 
 from __future__ import annotations
@@ -199,7 +204,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--grad-pool-gb", type=float, default=48.0,
+                    help="device memory for pre-generated per-step gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0)
@@ -237,14 +244,20 @@ def main() -> int:
     dev = torch.device("cuda:0")
     u8 = torch.uint8
     params = torch.zeros(pbytes, dtype=u8, device=dev)
-    grads = torch.zeros(pbytes, dtype=u8, device=dev)
     state = torch.zeros(max(plan.state_bytes, 256), dtype=u8, device=dev)
     ws_bytes = max(plan.workspace_bytes, 256)
     ws = torch.zeros(ws_bytes, dtype=u8, device=dev)
-    W.fill(wl, 1, params, grads, params_too=True)
+    # a fresh seeded gradient per step (step t of the run draws the workload's
+    # gradient stream t), generated before anything is timed
+    n_grad = max(1, min(1 + args.warmup + args.steps, int(args.grad_pool_gb * 1e9 // pbytes)))
+    grad_pool = [torch.zeros(pbytes, dtype=u8, device=dev) for _ in range(n_grad)]
+    W.fill(wl, 1, params, grad_pool[0], params_too=True)
+    for j in range(1, n_grad):
+        W.fill(wl, j + 1, params, grad_pool[j], params_too=False)
     torch.cuda.synchronize()
     log(f"[bench] {wl.name}: {len(wl.muon_specs())} Muon matrices, params {pbytes / 1e9:.2f} GB, "
-        f"state {plan.state_bytes / 1e9:.2f} GB, workspace {ws_bytes / 1e9:.2f} GB, plan {plan_ms:.1f} ms")
+        f"state {plan.state_bytes / 1e9:.2f} GB, workspace {ws_bytes / 1e9:.2f} GB, "
+        f"{n_grad} gradient buffers, plan {plan_ms:.1f} ms")
 
     hip = HipEvents()
     n_ev = plan.num_events()
@@ -252,6 +265,7 @@ def main() -> int:
     stream = torch.cuda.current_stream().cuda_stream
 
     def one(step, events=(), resident=True):
+        grads = grad_pool[(step - 1) % n_grad]
         plan.step(params.data_ptr(), grads.data_ptr(), state.data_ptr(), ws.data_ptr(), ws_bytes, step,
                   stream=stream, flags=B.STEP_DESCRIPTORS_RESIDENT if resident else 0, events=events)
 
@@ -406,13 +420,14 @@ def main() -> int:
         "config": {"workload": wl.name, "muon_matrices": len(specs), "muon_elements": muon_el,
                    "tail_tensors": sum(1 for s in wl.specs if s not in specs and s.numel > 0),
                    "tail_elements": tail_el, "ns_steps": steps_ns, "momentum_dtype": args.momentum_dtype,
-                   "parallelism": "single GPU owner"},
+                   "fresh_gradient_buffers": n_grad, "parallelism": "single GPU owner"},
         "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
         "step_ms_p90": round(sorted(step_ms)[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4),
         "step_ms_all": [round(x, 4) for x in step_ms],
         "matrices_per_s": round(len(specs) / (ms * 1e-3), 2),
         "ns_tflops_nominal": round(nominal / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "ns_frac_peak": round(nominal / (ns_ms * 1e-3) / 1e12 / peak, 4) if ns_ms else None,
+        "ns_meets_60pct_target": (nominal / (ns_ms * 1e-3) / 1e12 / peak >= 0.60) if ns_ms else None,
         "ns_tflops_executed": round(executed_ns_flops() / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "step_tflops_nominal": round(nominal / (ms * 1e-3) / 1e12, 2),
         "phases_ms": {"adamw": round(adam_ms, 4), "momentum_norm": round(mom_ms, 4), "ns_total": round(ns_ms, 4),
@@ -424,7 +439,13 @@ def main() -> int:
                         "copy_ceiling_gbs": round(copy_gbs, 1),
                         "hbm_stream_probe": hbm,
                         "momentum_frac_copy_ceiling": round(k1_bytes / (mom_ms * 1e-3) / 1e9 / copy_gbs, 4) if mom_ms else None,
-                        "adamw_gbs": round(tail_bytes / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None},
+                        "adamw_gbs": round(tail_bytes / (adam_ms * 1e-3) / 1e9, 1) if adam_ms and tail_el else None,
+                        # the target is 70% of the published 8 TB/s; the copy-ceiling fraction above
+                        # says how close the pass is to what a read+write stream reaches here, not that
+                        # the target is met
+                        "target_frac_hbm": 0.70,
+                        "momentum_meets_target": (k1_bytes / (mom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS >= 0.70)
+                        if mom_ms else None},
         "roofline": roofline,
         "cpu_baseline": None,
     }
