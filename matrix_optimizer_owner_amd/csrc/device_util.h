@@ -12,14 +12,21 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byt
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// float -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet
-// NaN.  Branch-free (a select), so it does not diverge inside epilogues.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t quiet = (u >> 16) | 0x40u;
-    return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 packed in one word (lo in bits 15:0), round to
+// nearest, ties to even, by gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32: one instruction for both values, where a software
+// rounding takes about six).  Finite values, denormals and infinities round
+// exactly as round-to-nearest-even defines (checked against a software
+// rounding on every fp32 bit pattern); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+// One float -> bfloat16 bits, as pack_bf16x2.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // Storage-type traits of the Newton-Schulz buffers: uint16_t holds bf16 bits.
 template <typename T> struct Store;

@@ -62,10 +62,10 @@ template <typename T> struct Vec8;  // eight elements of the Newton-Schulz (or m
 template <> struct Vec8<uint16_t> {
     __device__ static void store(uint16_t* p, const float* u) {
         uint4 v;
-        v.x = uint32_t(f32_to_bf16(u[0])) | (uint32_t(f32_to_bf16(u[1])) << 16);
-        v.y = uint32_t(f32_to_bf16(u[2])) | (uint32_t(f32_to_bf16(u[3])) << 16);
-        v.z = uint32_t(f32_to_bf16(u[4])) | (uint32_t(f32_to_bf16(u[5])) << 16);
-        v.w = uint32_t(f32_to_bf16(u[6])) | (uint32_t(f32_to_bf16(u[7])) << 16);
+        v.x = pack_bf16x2(u[0], u[1]);
+        v.y = pack_bf16x2(u[2], u[3]);
+        v.z = pack_bf16x2(u[4], u[5]);
+        v.w = pack_bf16x2(u[6], u[7]);
         *reinterpret_cast<uint4*>(p) = v;
     }
 };

@@ -99,8 +99,8 @@ template <> struct Vec4<uint16_t> {
     }
     __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[4]) {
         uint2 w;
-        w.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-        w.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(p) = w;
     }
 };
@@ -246,8 +246,8 @@ __device__ __forceinline__ void w_update4(WT_* w, float* o_out, const float* o, 
         for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(-step, o[e], __builtin_fmaf(-lrwd, wv[e], wv[e]));
         if constexpr (sizeof(WT_) == 2) {
             uint2 raw;
-            raw.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
-            raw.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
+            raw.x = pack_bf16x2(r[0], r[1]);
+            raw.y = pack_bf16x2(r[2], r[3]);
             *reinterpret_cast<uint2*>(w) = raw;
         } else {
             *reinterpret_cast<float4*>(w) = make_float4(r[0], r[1], r[2], r[3]);
@@ -506,6 +506,55 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
             }
         }
         __syncthreads();  // the staging area is free for the next pass
+    }
+}
+
+// Update epilogue for bf16 X'^T when the main loop has already added a X (the
+// 256-tile locked loop): every wave converts its block of accumulators to
+// bf16 (times s on a first iteration) and writes it into LDS in X'^T order,
+// all four waves at once (the whole tile in bf16 is BT * BT * 2 = 128 KB),
+// then the block walks the tile in 16-byte chunks: each lane reads 8
+// consecutive X'^T elements of one row from LDS and stores them, so a wave
+// instruction covers two whole 512-byte rows.  Staged row R (local n index)
+// holds BT/8 granules of 16 bytes; logical granule j sits at j ^ (R % 32).
+// A half-wave's 32 lanes write the same 8-byte half of the same m granule of
+// 32 consecutive rows, which the XOR spreads over 32 distinct granules (all
+// banks), and a lane's 8-byte write and its 16-byte read each stay inside
+// one granule.  Same values as the two-pass fp32 staging (one fp32 multiply
+// by s, then round to nearest even), with half the LDS traffic and half the
+// store instructions.
+template <int BT, int NW>
+__device__ __forceinline__ void update_epilogue_bf16(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                                     const MatDesc& d, int row0, int col0, int wm, int wn, int frow,
+                                                     int fhalf, float s1, uint16_t* XTout, uint8_t* lds_raw) {
+    using S = Shape<BT, NW>;
+    constexpr int RB = BT * 2;              // bytes of one staged row
+    constexpr int GPR = BT / 8;             // 16-byte granules per staged row
+    constexpr int NIT = BT * GPR / S::kThreads;
+    static_assert(GPR >= 32 && (BT * GPR) % S::kThreads == 0, "walk");
+    __syncthreads();  // every wave is done with the operand stages
+#pragma unroll
+    for (int mi = 0; mi < S::MM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < S::MN; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rl = wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;  // local m index, 4 consecutive
+                const int cl = wn * S::WTN + ni * 32 + frow;               // staged row (local n index)
+                const int g = (rl >> 3) ^ (cl & 31);
+                uint2 w;
+                w.x = pack_bf16x2(acc[mi][ni][q * 4] * s1, acc[mi][ni][q * 4 + 1] * s1);
+                w.y = pack_bf16x2(acc[mi][ni][q * 4 + 2] * s1, acc[mi][ni][q * 4 + 3] * s1);
+                *reinterpret_cast<uint2*>(lds_raw + cl * RB + g * 16 + ((rl >> 2) & 1) * 8) = w;
+            }
+    __syncthreads();
+    const uint32_t ld = uint32_t(d.ld);
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int k = threadIdx.x + i * S::kThreads;
+        const int R = k / GPR, j = k % GPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + R * RB + (j ^ (R & 31)) * 16);
+        *reinterpret_cast<uint4*>(XTout + (uint32_t(col0 + R) * ld + uint32_t(row0 + j * 8))) = v;
     }
 }
 
@@ -883,6 +932,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         const uint16_t amid = f32_to_bf16(ar1);
         const uint16_t alo = f32_to_bf16(ar1 - bf16_to_f32(amid));
         auto fold = [&](auto blk, auto ro, const u32x4_t (&fb)[MN]) {
+          // (instantiated only where the fold is used: 256-tiles, MM = 4)
+          if constexpr (kFoldAX) {
             int t = frow - 16 * decltype(ro)::value - 8 * fhalf;
             asm volatile("" : "+v"(t));  // keeps the fragments out of loop-invariant hoisting
             u32x4_t ih, im, il;
@@ -900,6 +951,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 #pragma unroll
             for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], il, fb[jj]);
             __builtin_amdgcn_sched_barrier(0);
+          }
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
@@ -1064,8 +1116,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                                 reinterpret_cast<float*>(lds_raw));
         return;
     } else if constexpr (PHASE == kUpdate) {
-        update_epilogue<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
-                                   reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0])), lds_raw);
+        T* XTout = reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0]));
+        if constexpr (kFoldAX && sizeof(T) == 2)
+            update_epilogue_bf16<BT, NW>(acc, d, row0, col0, wm, wn, frow, fhalf, s1, XTout, lds_raw);
+        else
+            update_epilogue<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, XTout, lds_raw);
         return;
     } else {
         // Gram / polynomial: the tile and (off the diagonal) its mirror
