@@ -558,6 +558,114 @@ __device__ __forceinline__ void update_epilogue_bf16(const f32x16_t (&acc)[Shape
     }
 }
 
+// Gram / polynomial epilogue, bf16: the tile C (rows r of the tile's row
+// block, columns c of its column block; Gram C = s^2 acc, polynomial C = b A
+// + c acc) is stored twice in the symmetric output, at (r, c) and at the
+// mirror position (c, r).  A lane's accumulators hold 4 consecutive rows r
+// of one column c, which are 4 consecutive elements of mirror row c, so the
+// mirror store goes straight from registers (8 bytes per lane).  A diagonal
+// tile is its own mirror (C is exactly symmetric there: element (r, c) and
+// element (c, r) are the same products summed in the same order), so that
+// store alone writes the whole tile.  Off the diagonal the (r, c)
+// orientation is staged in LDS as a row-major bf16 tile (2-byte writes, one
+// per element; BT * BT * 2 bytes) and then walked in 16-byte chunks, so a
+// wave instruction stores whole output rows.  Staged row r holds BT/8
+// granules of 16 bytes, logical granule g at g ^ ((r / 4) % (BT/8)): the 32
+// lanes of a half-wave write 64 consecutive bytes of one row, the four rows
+// of a lane's accumulator group share one swizzle (one address, constant
+// offsets), and a quarter-wave's 16-byte reads of one row hit distinct
+// banks.  This replaces an
+// in-register 4 x 4 transpose whose lane-dependent selects cost about 1,500
+// VALU instructions per wave on 256-tiles.  The polynomial's A (for b A) is
+// read along A's transposed layout (A is symmetric), one MFMA row block
+// ahead, where a lane's 4 rows are 4 consecutive elements.
+template <int PHASE, int BT, int NW>
+__device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
+                                                        const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm,
+                                                        int wn, int frow, int fhalf, float s1, bool diag,
+                                                        uint8_t* lds_raw) {
+    using S = Shape<BT, NW>;
+    constexpr int MM = S::MM, MN = S::MN;
+    constexpr int RB = BT * 2;              // bytes of one staged row
+    constexpr int GPR = BT / 8;             // 16-byte granules per staged row
+    constexpr int NIT = BT * GPR / S::kThreads;
+    static_assert((BT * GPR) % S::kThreads == 0 && GPR >= 4, "walk");
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.ws + (PHASE == kGram ? d.a_off : d.b_off));
+    const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
+    const uint32_t ld = uint32_t(d.ld);
+    const float s2 = s1 * s1;
+    // per lane: its first local row (the 4 rows of an accumulator group sit
+    // at + mi*32 + q*8 .. +3) and, per column block ni, its local column
+    const int rl0 = wm * S::WTM + fhalf * 4;
+    // mirror row c = col0 + cl, from element row0 + rl0 on (A and B share
+    // the layout, so this offset also addresses the polynomial's A)
+    const uint32_t moff0 = uint32_t(col0 + wn * S::WTN + frow) * ld + uint32_t(row0 + rl0);
+    auto moff = [&](int ni) { return moff0 + uint32_t(ni * 32) * ld; };
+    uint2 ev[2][MN][4];
+    if constexpr (PHASE == kPoly) {
+#pragma unroll
+        for (int ni = 0; ni < MN; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ev[0][ni][q] = *reinterpret_cast<const uint2*>(E + moff(ni) + q * 8);
+    }
+    if (!diag) __syncthreads();  // every wave is done with the operand stages (block-uniform branch)
+#pragma unroll
+    for (int mi = 0; mi < MM; ++mi) {
+        if constexpr (PHASE == kPoly) {
+            if (mi + 1 < MM) {
+#pragma unroll
+                for (int ni = 0; ni < MN; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        ev[(mi + 1) & 1][ni][q] =
+                            *reinterpret_cast<const uint2*>(E + moff(ni) + (mi + 1) * 32 + q * 8);
+            }
+        }
+#pragma unroll
+        for (int ni = 0; ni < MN; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rl = rl0 + mi * 32 + q * 8;        // local row of the first of 4
+                const int cl = wn * S::WTN + ni * 32 + frow;  // local column
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (PHASE == kGram) {
+                        v[e] = acc[mi][ni][q * 4 + e] * s2;
+                    } else {
+                        const uint2 r = ev[mi & 1][ni][q];
+                        const uint32_t w = e < 2 ? r.x : r.y;
+                        const float ae = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+                        v[e] = a.cb * ae + a.cc * acc[mi][ni][q * 4 + e];
+                    }
+                }
+                uint2 pk;
+                pk.x = pack_bf16x2(v[0], v[1]);
+                pk.y = pack_bf16x2(v[2], v[3]);
+                // mirror position (c, r .. r+3): 4 consecutive elements of row c
+                *reinterpret_cast<uint2*>(out + moff(ni) + mi * 32 + q * 8) = pk;
+                if (!diag) {
+                    // rows rl .. rl+3 (rl a multiple of 4) share the swizzle
+                    // key rl/4, so the four writes share one address
+                    uint8_t* p = lds_raw + rl * RB + (((cl >> 3) ^ ((rl >> 2) & (GPR - 1))) * 16) + (cl & 7) * 2;
+                    *reinterpret_cast<uint16_t*>(p) = uint16_t(pk.x);
+                    *reinterpret_cast<uint16_t*>(p + RB) = uint16_t(pk.x >> 16);
+                    *reinterpret_cast<uint16_t*>(p + 2 * RB) = uint16_t(pk.y);
+                    *reinterpret_cast<uint16_t*>(p + 3 * RB) = uint16_t(pk.y >> 16);
+                }
+            }
+    }
+    if (diag) return;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int k = threadIdx.x + i * S::kThreads;
+        const int R = k / GPR, jg = k % GPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + R * RB + ((jg ^ ((R >> 2) & (GPR - 1))) * 16));
+        *reinterpret_cast<uint4*>(out + (uint32_t(row0 + R) * ld + uint32_t(col0 + jg * 8))) = v;
+    }
+}
+
 // Scheduling groups for one stage of the main loop (bf16), in program order:
 // the stage's direct-to-LDS loads and the previous stage's deferred last
 // sub-step of MFMAs, interleaved with sub-step 1's fragment reads; then for
@@ -1121,6 +1229,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             update_epilogue_bf16<BT, NW>(acc, d, row0, col0, wm, wn, frow, fhalf, s1, XTout, lds_raw);
         else
             update_epilogue<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, XTout, lds_raw);
+        return;
+    } else if constexpr (sizeof(T) == 2) {
+        gram_poly_epilogue_bf16<PHASE, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1,
+                                                uni(int(tile.ti) - int(tile.tj)) == 0, lds_raw);
         return;
     } else {
         // Gram / polynomial: the tile and (off the diagonal) its mirror
