@@ -220,6 +220,31 @@ mfsdp_status mfsdp_owner_step(mfsdp_plan_t plan, const mfsdp_step_args* args);
  * with capacity > 0). */
 mfsdp_status mfsdp_plan_regions(mfsdp_plan_t plan, mfsdp_region* regions, int64_t capacity, int64_t* count);
 
+/* ---- A step that allocates nothing ----
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * step as mfsdp_owner_step (same kernels, bitwise the same results), except
+ * that the workspace is a fixed array inside the library: a file-scope
+ * device array of MFSDP_STATIC_WORKSPACE_BYTES, which every GPU the library
+ * runs on holds until the process ends.  The caller still passes params,
+ * grads, state, ns_out and events as for mfsdp_owner_step, with workspace =
+ * NULL and workspace_bytes = 0.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); on its first call on a device it
+ * looks up that device's copy of the array (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  The step writes every workspace
+ * byte before it reads it, so nothing is cleared between calls.
+ * MFSDP_STEP_DESCRIPTORS_RESIDENT skips the descriptor upload only when the
+ * previous static call on this device used the same plan.
+ * Errors: those of mfsdp_owner_step, plus INVALID_ARGUMENT (workspace not
+ * NULL or workspace_bytes not 0), WORKSPACE_TOO_SMALL (the plan needs more
+ * than MFSDP_STATIC_WORKSPACE_BYTES: use mfsdp_owner_step), UNSUPPORTED
+ * (device index 64 or more), HIP. */
+#define MFSDP_STATIC_WORKSPACE_BYTES (64ull << 20)
+mfsdp_status mfsdp_owner_step_static(mfsdp_plan_t plan, const mfsdp_step_args* args);
+
 /* Free a plan.  NULL is accepted. */
 mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
 

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmfsdp.so")
 F32, BF16 = 0, 1
 ROLE_AUTO, ROLE_MUON, ROLE_ADAMW = 0, 1, 2
 STEP_DESCRIPTORS_RESIDENT = 1
+STATIC_WORKSPACE_BYTES = 64 << 20  # MFSDP_STATIC_WORKSPACE_BYTES
 
 STATUS = {
     0: "MFSDP_OK",
@@ -91,7 +92,7 @@ class TensorPlace(ctypes.Structure):
 EXPORTS = (
     "mfsdp_plan_create", "mfsdp_plan_state_bytes", "mfsdp_plan_workspace_bytes", "mfsdp_plan_ns_out_elems",
     "mfsdp_plan_num_events", "mfsdp_plan_num_entries", "mfsdp_plan_entry_info", "mfsdp_plan_regions",
-    "mfsdp_owner_step", "mfsdp_plan_destroy",
+    "mfsdp_owner_step", "mfsdp_owner_step_static", "mfsdp_plan_destroy",
     "mfsdp_owner_partition", "mfsdp_owner_gather", "mfsdp_owner_scatter", "mfsdp_status_string",
     "mfsdp_last_error_message", "mfsdp_probe_mfma_bf16", "mfsdp_probe_hbm",
 )
@@ -119,6 +120,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfsdp_plan_entry_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(EntryInfo)]
     lib.mfsdp_plan_regions.argtypes = [P, ctypes.POINTER(Region), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
     lib.mfsdp_owner_step.argtypes = [P, ctypes.POINTER(StepArgs)]
+    lib.mfsdp_owner_step_static.argtypes = [P, ctypes.POINTER(StepArgs)]
     lib.mfsdp_plan_destroy.argtypes = [P]
     lib.mfsdp_owner_partition.argtypes = [ctypes.POINTER(Tensor), ctypes.c_int64, ctypes.POINTER(PartitionParams),
                                           ctypes.POINTER(TensorPlace), ctypes.POINTER(ctypes.c_double), u64p, u64p]
@@ -244,6 +246,15 @@ class OwnerPlan:
         args = StepArgs(params, grads, state, workspace, workspace_bytes, step, stream or None, ns_out or None, flags,
                         ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None, len(events))
         _check(self._lib.mfsdp_owner_step(self._h, ctypes.byref(args)))
+
+    def step_static(self, params: int, grads: int, state: int, step: int, stream: int = 0, ns_out: int = 0,
+                    flags: int = 0, events: Sequence[int] = ()) -> None:
+        """mfsdp_owner_step_static: the step on the library's own workspace
+        (no allocation; at most STATIC_WORKSPACE_BYTES of workspace)."""
+        ev = (ctypes.c_void_p * len(events))(*events) if events else None
+        args = StepArgs(params, grads, state, None, 0, step, stream or None, ns_out or None, flags,
+                        ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None, len(events))
+        _check(self._lib.mfsdp_owner_step_static(self._h, ctypes.byref(args)))
 
     def _ptrs(self, addrs):
         if addrs is None:

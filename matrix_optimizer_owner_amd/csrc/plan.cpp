@@ -8,6 +8,7 @@
 // non-matrix tail to AdamW (Abstract), with empty shards legal (Abstract:
 // non-owners hold empty shards).
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -114,6 +115,8 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
 
     mfsdp_plan_s* plan = new (std::nothrow) mfsdp_plan_s();
     if (!plan) return fail(MFSDP_ERR_INTERNAL, "out of host memory");
+    static std::atomic<uint64_t> next_id{1};
+    plan->id = next_id.fetch_add(1);
     try {
         plan->entries.assign(entries, entries + n);
         plan->hp = *hp;

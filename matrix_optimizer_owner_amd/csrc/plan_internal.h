@@ -17,6 +17,7 @@ struct mfsdp_plan_s {
     uint64_t state_bytes = 0;
     uint64_t ns_out_elems = 0;
     uint64_t max_param_end = 0;       // highest byte any entry touches
+    uint64_t id = 0;                  // unique per plan in the process (never 0)
 };
 
 namespace mfsdp {
