@@ -1156,7 +1156,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             mfmas(fa1, fb1);  // last sub-step of the last stage
             wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
         };
-        if constexpr (PHASE == kGram || PHASE == kPoly) {
+        // Not for the Gram on 256-tiles: there a diagonal tile would finish
+        // early (K = n is long) and its CU would start the next tile group
+        // while the rest of its group still streams the strips they share,
+        // so the 32 tiles an XCD runs together drift apart and re-fetch
+        // evicted strips.  On the mixed 256-matrix set that took the Gram's
+        // L2 misses from 28 to 65 GB per launch and its time up 5%.
+        if constexpr (PHASE == kPoly || (PHASE == kGram && BT == 128)) {
             if (uni(int(tile.ti) - int(tile.tj)) == 0)
                 run(std::true_type{});
             else
