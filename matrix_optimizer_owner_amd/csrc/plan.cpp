@@ -64,17 +64,23 @@ double shape_scale(int64_t rows, int64_t cols, int mode) {
     return 0.2 * std::sqrt(double(std::max(rows, cols)));
 }
 
-// Tiles of one matrix for one phase in 2D chunks of kChunkRows x kChunkCols
-// tiles (upper-triangle tiles only for the symmetric phases).  A chunk is what
-// one XCD works on at a time, so the operand panels it touches are few and
-// shared through that XCD's L2.
-constexpr int kChunkRows = 8, kChunkCols = 4, kChunk = kChunkRows * kChunkCols, kXcds = 8;
+// Tiles of one matrix for one phase in 2D chunks of cr x cc tiles
+// (upper-triangle tiles only for the symmetric phases).  A chunk is what one
+// XCD works on at a time, so the operand panels it touches are few and
+// shared through that XCD's L2: cr + cc panels for cr * cc = 32 tiles.  The
+// symmetric phases use 8 x 4, the update 4 x 8 (4 row panels of B, 8 of
+// X^T): with 8 x 4 the mixed 256-matrix set's update missed the L2 for 67 GB
+// per launch, with 4 x 8 for 50 GB, at the same speed (8B share 1% faster).
+constexpr int kChunk = 32, kXcds = 8;
+constexpr int kTriChunkRows = 8, kTriChunkCols = 4, kUpdChunkRows = 4, kUpdChunkCols = 8;
+static_assert(kTriChunkRows * kTriChunkCols == kChunk && kUpdChunkRows * kUpdChunkCols == kChunk, "chunk size");
 
 void emit_tiles(std::vector<Tile>& out, uint32_t mat, int tm, int tn, bool upper) {
-    for (int r0 = 0; r0 < tm; r0 += kChunkRows)
-        for (int c0 = upper ? (r0 / kChunkCols) * kChunkCols : 0; c0 < tn; c0 += kChunkCols)
-            for (int tj = c0; tj < std::min(tn, c0 + kChunkCols); ++tj)
-                for (int ti = r0; ti < std::min(tm, r0 + kChunkRows); ++ti) {
+    const int cr = upper ? kTriChunkRows : kUpdChunkRows, cc = upper ? kTriChunkCols : kUpdChunkCols;
+    for (int r0 = 0; r0 < tm; r0 += cr)
+        for (int c0 = upper ? (r0 / cc) * cc : 0; c0 < tn; c0 += cc)
+            for (int tj = c0; tj < std::min(tn, c0 + cc); ++tj)
+                for (int ti = r0; ti < std::min(tm, r0 + cr); ++ti) {
                     if (upper && ti > tj) continue;
                     out.push_back(Tile{mat, uint16_t(ti), uint16_t(tj)});
                 }
