@@ -67,12 +67,14 @@ double shape_scale(int64_t rows, int64_t cols, int mode) {
 // Tiles of one matrix for one phase in 2D chunks of cr x cc tiles
 // (upper-triangle tiles only for the symmetric phases).  A chunk is what one
 // XCD works on at a time, so the operand panels it touches are few and
-// shared through that XCD's L2: cr + cc panels for cr * cc = 32 tiles.  The
-// symmetric phases use 8 x 4, the update 4 x 8 (4 row panels of B, 8 of
-// X^T): with 8 x 4 the mixed 256-matrix set's update missed the L2 for 67 GB
-// per launch, with 4 x 8 for 50 GB, at the same speed (8B share 1% faster).
+// shared through that XCD's L2: cr + cc panels for cr * cc = 32 tiles.
+// Every phase uses 4 x 8 (for the update, 4 row panels of B and 8 of X^T).
+// Against 8 x 4, which counts as many panels per chunk, the mixed 256-matrix
+// set's update missed the L2 for 50 GB per launch instead of 67 at the same
+// speed, its Gram for 27 GB instead of 29, and the Gram and polynomial ran
+// 0.4-1% faster on the three large workloads.
 constexpr int kChunk = 32, kXcds = 8;
-constexpr int kTriChunkRows = 8, kTriChunkCols = 4, kUpdChunkRows = 4, kUpdChunkCols = 8;
+constexpr int kTriChunkRows = 4, kTriChunkCols = 8, kUpdChunkRows = 4, kUpdChunkCols = 8;
 static_assert(kTriChunkRows * kTriChunkCols == kChunk && kUpdChunkRows * kUpdChunkCols == kChunk, "chunk size");
 
 void emit_tiles(std::vector<Tile>& out, uint32_t mat, int tm, int tn, bool upper) {
