@@ -175,7 +175,7 @@ def cpu_baseline_tail(wl, hp, budget_s: float, cores: int):
 # for the kernel sources they were taken with.
 TRAFFIC = {
     # (workload, precision, phase): (sources sha256[:16], fetch bytes, write bytes)
-    ("llama3-8b-owner-share-4L", "bf16", "update"): ("a99acbac78d04d8f", 10177552656, 1744830464),
+    ("mixed-256-stress", "bf16", "update"): ("c87b5a183628007c", 49768865178, 9145679872),
 }
 TRAFFIC_SOURCES = ("matrix_optimizer_owner_amd/csrc/ns_gemm.hip", "matrix_optimizer_owner_amd/csrc/plan.cpp",
                    "matrix_optimizer_owner_amd/csrc/layout.h")
