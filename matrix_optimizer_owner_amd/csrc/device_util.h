@@ -39,6 +39,21 @@ template <> struct Store<float> {
     __device__ __forceinline__ static float cvt(float f) { return f; }
 };
 
+// Element offsets into a Newton-Schulz buffer of ld columns stored in panel
+// blocks of 256 rows x 128 bytes (CB columns of T; layout.h describes the
+// layout).  Offsets fit in 32 bits: the planner keeps every buffer below
+// 2 GiB.
+template <typename T> struct Panel {
+    static constexpr int CB = 128 / int(sizeof(T));  // columns per block
+    static constexpr int BE = 256 * CB;              // elements per block
+    // element (r, c)
+    __device__ __forceinline__ static uint32_t off(int r, int c, int ld) {
+        return uint32_t((r >> 8) * (ld / CB) + c / CB) * uint32_t(BE) + uint32_t((r & 255) * CB + (c % CB));
+    }
+    // from element (r, c) with c % CB == 0 to (r, c + dc), 0 <= dc
+    __host__ __device__ static constexpr uint32_t dcol(int dc) { return uint32_t(dc / CB) * BE + uint32_t(dc % CB); }
+};
+
 // Parameter / gradient element access by runtime dtype (0 = fp32, 1 = bf16).
 __device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t i) {
     return dtype == 1 ? bf16_to_f32(static_cast<const uint16_t*>(base)[i]) : static_cast<const float*>(base)[i];

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
     const int local = blk - a.k1_begin[mi];
     const int tr = local / d.k1_tiles_c, tc = local % d.k1_tiles_c;
     const int R = d.rows, C = d.cols;  // natural shape
-    T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);  // np rows of ld
+    T* xt0 = reinterpret_cast<T*>(a.ws + d.x_off[0]);  // np rows of ld, panel blocks
     const bool tall = d.transposed != 0;
     const uint8_t* g = a.grads + d.param_off;
     MT* mom = reinterpret_cast<MT*>(a.state + d.mom_off);
@@ -171,10 +171,13 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
             }
         }
     }
+    // (8 consecutive X0^T elements from a multiple of 8 stay inside one
+    // 128-byte row of a panel block)
+    const int ld = int(d.ld);
     if (tall) {
         // X0^T is the natural layout: natural row r -> X0^T row r
 #pragma unroll
-        for (int i = 0; i < SUB; ++i) Vec8<T>::store(xt0 + int64_t(r0 + i) * d.ld + c0, u[i]);
+        for (int i = 0; i < SUB; ++i) Vec8<T>::store(xt0 + Panel<T>::off(r0 + i, c0, ld), u[i]);
     } else {
         // X0^T row = natural column c0 + k, elements r0 .. r0 + 7
 #pragma unroll
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(256) void k_momentum(MomentumArgs a) {
             float col[SUB];
 #pragma unroll
             for (int i = 0; i < SUB; ++i) col[i] = u[i][k];
-            Vec8<T>::store(xt0 + int64_t(c0 + k) * d.ld + r0, col);
+            Vec8<T>::store(xt0 + Panel<T>::off(c0 + k, r0, ld), col);
         }
     }
 
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256) void k_final_from_x(FinalArgs a) {
         const int r = tr * kK1Tile + e / kK1Tile, c = tc * kK1Tile + e % kK1Tile;
         if (r >= d.rows || c >= d.cols) continue;
         // natural (r, c) is X0^T[r][c] for a tall matrix, X0^T[c][r] for a wide one
-        const int64_t xi = d.transposed ? int64_t(r) * d.ld + c : int64_t(c) * d.ld + r;
+        const uint32_t xi = d.transposed ? Panel<T>::off(r, c, int(d.ld)) : Panel<T>::off(c, r, int(d.ld));
         const float o = s * Store<T>::load(xt0 + xi);
         const int64_t idx = int64_t(r) * d.cols + c;
         const float wv = load_elem(w, d.dtype, idx);

@@ -8,16 +8,30 @@
 //   [s]         float[n_mat]: 1/(||U||_F + eps) per Muon matrix
 //   [partials]  float[n_k1_blocks]: sum of u^2 over one momentum-kernel tile
 //   per matrix: XT0 and XT1 (np x mp, ping-pong), A and B (mp x mp) in the
-//               Newton-Schulz storage type (bf16 or fp32), row-major with
-//               row pitch ld = mp + kLdPad elements.
+//               Newton-Schulz storage type (bf16 or fp32), in panel blocks
+//               (below); ld = mp columns.
+//
+// Panel blocks: a Newton-Schulz buffer of R rows and ld columns (R and ld
+// multiples of 256) is stored as (R/256) x (ld*es/128) blocks of 256 rows x
+// 128 bytes (CB = 128/es columns), each block contiguous (32 KB) with its
+// rows at a 128-byte pitch, blocks in row-major order: element (r, c) sits at
+// element offset ((r/256) * (ld/CB) + c/CB) * 256*CB + (r%256) * CB + c%CB.
+// One stage of a contraction tile (256 or 128 rows x 128 bytes of the
+// contraction index) is then one contiguous piece of a block.  With a plain
+// row-major layout each of a stage's rows was a separate 128-byte piece at a
+// pitch of ld elements: on the mixed 256-matrix set the update's main loop
+// then took 2870 shader cycles per stage (2048 of them MFMA), against 2590
+// from contiguous pieces.  Its MFMA pipes went from 72% to 75% busy, but
+// the power-limited clock fell from 1.63 to 1.56 GHz, so the update gained
+// only 1-3% in time.
 //
 // Orientation: every Muon matrix is handled as X (m x n, m <= n).  A tall
 // matrix (rows > cols) is stored transposed.  m and n are padded to
 // multiples of kPad with zeros; the zeros stay zero through every
 // Newton-Schulz iteration (rows and columns of zeros map to zeros), so the
 // contraction kernels need no bounds checks.  X is kept only as X^T
-// (row-major n x m): the update reads it along its rows (the contraction
-// index m), the Gram reads it K-major through the transposing LDS read.
+// (n x m): the update reads it along its rows (the contraction index m), the
+// Gram reads it K-major through the transposing LDS read.
 #pragma once
 #include <stdint.h>
 
@@ -30,13 +44,8 @@ constexpr int kLargeTileMin = 512; // a phase uses 256-tiles when it has at leas
 constexpr int kCus = 256;          // compute units of the part (one 256-tile block each)
 constexpr int kSplitTailMax = 64;  // a last update round of at most this many 256-tiles runs as 128-tiles
 constexpr int kK1Tile = 128;       // tile edge of the momentum kernel
-// Row pitch pad (elements) of the Newton-Schulz buffers beyond mp.  Pads of
-// 64 and 128 elements (against the power-of-two pitch of most shapes)
-// measured no faster on the Llama-3-8B share; unaligned pads were slower.
-#ifndef MFSDP_LDPAD
-#define MFSDP_LDPAD 0
-#endif
-constexpr int kLdPad = MFSDP_LDPAD;
+constexpr int kBlockRows = 256;    // rows of a panel block of the Newton-Schulz buffers
+constexpr int kBlockBytes = 128;   // bytes of a panel block's row
 constexpr int kTailChunk = 2048;   // elements per AdamW block
 constexpr uint64_t kAlign = 256;
 
@@ -45,10 +54,10 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 struct MatDesc {
     uint64_t param_off;    // bytes into params and grads
     uint64_t mom_off;      // bytes into state (fp32 momentum, rows x cols)
-    uint64_t x_off[2];     // bytes into workspace: X^T ping-pong (np rows of ld, row-major)
-    int64_t ld;            // row pitch (elements) of the X^T, A and B buffers: mp + kLdPad
-    uint64_t a_off;        // bytes into workspace: A  (mp rows of ld)
-    uint64_t b_off;        // bytes into workspace: B  (mp rows of ld)
+    uint64_t x_off[2];     // bytes into workspace: X^T ping-pong (np rows of ld, panel blocks)
+    int64_t ld;            // columns (elements) of the X^T, A and B buffers: mp
+    uint64_t a_off;        // bytes into workspace: A  (mp rows of ld, panel blocks)
+    uint64_t b_off;        // bytes into workspace: B  (mp rows of ld, panel blocks)
     uint64_t ns_out_off;   // element offset into ns_out (fp32, rows x cols)
     int32_t rows, cols;    // shape as given
     int32_t m, n;          // oriented, m <= n

@@ -25,11 +25,13 @@
 // phases with too few large tiles to fill the chip.  Operands reach LDS by
 // direct global->LDS loads in 128-byte rows (64 bf16 or 32 fp32 of the
 // contraction index per stage) into split stage rings (3 slots for P, 2 for
-// Q).  bf16 runs a locked instruction schedule (MFMAs, fragment reads and
-// loads interleaved in a fixed order, over stage pairs) and, in the update
-// phases on 256 tiles, adds a X through identity-fragment MFMAs; fp32 runs a
-// compiler-scheduled loop.  Operands that are contiguous along
-// the contraction are read back with 16-byte fragment reads; the Gram's
+// Q); X^T, A and B are stored in panel blocks of 256 rows x 128 bytes, so a
+// stage of an operand tile is contiguous memory.  bf16 runs a locked
+// instruction schedule (MFMAs, fragment reads and loads interleaved in a
+// fixed order, over stage pairs) and, in the update phases on 256 tiles,
+// adds a X through identity-fragment MFMAs; fp32 runs a compiler-scheduled
+// loop.  Operands that are contiguous along the contraction are read back
+// with 16-byte fragment reads; the Gram's
 // K-major X^T is read back with the transposing LDS read
 // (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
 // v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
@@ -289,7 +291,7 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
     constexpr int PF = NPT * int(sizeof(Raw)) <= PFB ? NPT : PFB / int(sizeof(Raw));  // chunks per batch
     static_assert(CHUNKS % S::kThreads == 0 && NPT % PF == 0, "walk");
     const float step = d.lr_step;
-    const uint32_t ld = uint32_t(d.ld);  // row pitch of X^T
+    const int ld = int(d.ld);  // columns of X^T
     const int ldw = d.cols;
     float* O = a.ns_out ? a.ns_out + d.ns_out_off : nullptr;
     const int w_rows = d.rows, w_cols = d.cols;
@@ -345,7 +347,7 @@ __device__ __forceinline__ void final_update_t(const f32x16_t (&acc)[Shape<BT, N
                     for (int q = 0; q < 4; ++q) {
                         const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
                         const int c = col0 + wn * S::WTN + ni * 32 + frow;
-                        xv[ni][q] = Vec4<T>::load(XTin + (uint32_t(c) * ld + uint32_t(rb)));
+                        xv[ni][q] = Vec4<T>::load(XTin + Panel<T>::off(c, rb, ld));
                     }
             }
 #pragma unroll
@@ -454,14 +456,14 @@ __device__ __forceinline__ void update_epilogue(const f32x16_t (&acc)[Shape<BT, 
     static_assert(NCH >= 32, "swizzle range");
     static_assert((HB * NCH) % S::kThreads == 0, "walk");
     float* st = reinterpret_cast<float*>(lds_raw);
-    const int64_t ld = d.ld;  // row pitch of X^T and X'^T
+    const int ld = int(d.ld);  // columns of X^T and X'^T
     using Raw = typename Vec4<T>::raw;
     constexpr int PF = NPT * int(sizeof(Raw)) <= 256 ? NPT : 256 / int(sizeof(Raw));  // chunks per batch
     static_assert(NPT % PF == 0, "batches");
     Raw xv[PF];
-    auto gidx = [&](int h, int i) -> int64_t {
+    auto gidx = [&](int h, int i) -> uint32_t {
         const int k = threadIdx.x + i * S::kThreads;
-        return int64_t(col0 + h * HB + k / NCH) * ld + row0 + (k % NCH) * 4;
+        return Panel<T>::off(col0 + h * HB + k / NCH, row0 + (k % NCH) * 4, ld);
     };
     auto load_batch = [&](int h, int b) {
 #pragma unroll
@@ -548,13 +550,13 @@ __device__ __forceinline__ void update_epilogue_bf16(const f32x16_t (&acc)[Shape
                 *reinterpret_cast<uint2*>(lds_raw + cl * RB + g * 16 + ((rl >> 2) & 1) * 8) = w;
             }
     __syncthreads();
-    const uint32_t ld = uint32_t(d.ld);
+    const int ld = int(d.ld);
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
         const int k = threadIdx.x + i * S::kThreads;
         const int R = k / GPR, j = k % GPR;
         const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + R * RB + (j ^ (R & 31)) * 16);
-        *reinterpret_cast<uint4*>(XTout + (uint32_t(col0 + R) * ld + uint32_t(row0 + j * 8))) = v;
+        *reinterpret_cast<uint4*>(XTout + Panel<uint16_t>::off(col0 + R, row0 + j * 8, ld)) = v;
     }
 }
 
@@ -592,21 +594,24 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
     static_assert((BT * GPR) % S::kThreads == 0 && GPR >= 4, "walk");
     uint16_t* out = reinterpret_cast<uint16_t*>(a.ws + (PHASE == kGram ? d.a_off : d.b_off));
     const uint16_t* E = reinterpret_cast<const uint16_t*>(a.ws + d.a_off);
-    const uint32_t ld = uint32_t(d.ld);
+    const int ld = int(d.ld);
+    using PL = Panel<uint16_t>;
     const float s2 = s1 * s1;
     // per lane: its first local row (the 4 rows of an accumulator group sit
     // at + mi*32 + q*8 .. +3) and, per column block ni, its local column
     const int rl0 = wm * S::WTM + fhalf * 4;
     // mirror row c = col0 + cl, from element row0 + rl0 on (A and B share
-    // the layout, so this offset also addresses the polynomial's A)
-    const uint32_t moff0 = uint32_t(col0 + wn * S::WTN + frow) * ld + uint32_t(row0 + rl0);
-    auto moff = [&](int ni) { return moff0 + uint32_t(ni * 32) * ld; };
+    // the layout, so this offset also addresses the polynomial's A).  The
+    // wave's rows start at a multiple of a panel block's columns, and its
+    // mirror rows c .. c + 96 lie in one block row, 32*CB elements apart.
+    const uint32_t moff0 = PL::off(col0 + wn * S::WTN + frow, row0 + wm * S::WTM, ld) + uint32_t(fhalf * 4);
+    auto moff = [&](int ni) { return moff0 + uint32_t(ni * 32 * PL::CB); };
     uint2 ev[2][MN][4];
     if constexpr (PHASE == kPoly) {
 #pragma unroll
         for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ev[0][ni][q] = *reinterpret_cast<const uint2*>(E + moff(ni) + q * 8);
+            for (int q = 0; q < 4; ++q) ev[0][ni][q] = *reinterpret_cast<const uint2*>(E + moff(ni) + PL::dcol(q * 8));
     }
     if (!diag) __syncthreads();  // every wave is done with the operand stages (block-uniform branch)
 #pragma unroll
@@ -618,7 +623,7 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         ev[(mi + 1) & 1][ni][q] =
-                            *reinterpret_cast<const uint2*>(E + moff(ni) + (mi + 1) * 32 + q * 8);
+                            *reinterpret_cast<const uint2*>(E + moff(ni) + PL::dcol((mi + 1) * 32 + q * 8));
             }
         }
 #pragma unroll
@@ -643,7 +648,7 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
                 pk.x = pack_bf16x2(v[0], v[1]);
                 pk.y = pack_bf16x2(v[2], v[3]);
                 // mirror position (c, r .. r+3): 4 consecutive elements of row c
-                *reinterpret_cast<uint2*>(out + moff(ni) + mi * 32 + q * 8) = pk;
+                *reinterpret_cast<uint2*>(out + moff(ni) + PL::dcol(mi * 32 + q * 8)) = pk;
                 if (!diag) {
                     // rows rl .. rl+3 (rl a multiple of 4) share the swizzle
                     // key rl/4, so the four writes share one address
@@ -662,7 +667,7 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
         const int k = threadIdx.x + i * S::kThreads;
         const int R = k / GPR, jg = k % GPR;
         const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + R * RB + ((jg ^ ((R >> 2) & (GPR - 1))) * 16));
-        *reinterpret_cast<uint4*>(out + (uint32_t(row0 + R) * ld + uint32_t(col0 + jg * 8))) = v;
+        *reinterpret_cast<uint4*>(out + PL::off(row0 + R, col0 + jg * 8, ld)) = v;
     }
 }
 
@@ -788,19 +793,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
 
     const T* P;
     const T* Q;
-    int ldp, ldq, K;
+    int K;
     if (PHASE == kGram) {
         P = Q = XTin;
-        ldp = ldq = ld;
         K = np;
     } else if (PHASE == kPoly) {
         P = Q = reinterpret_cast<const T*>(a.ws + d.a_off);
-        ldp = ldq = ld;
         K = mp;
     } else {
         P = reinterpret_cast<const T*>(a.ws + d.b_off);
         Q = XTin;
-        ldp = ldq = ld;
         K = mp;
     }
 
@@ -829,10 +831,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     // column blocks of KST rows of 128 bytes: LDS row R = block*KST + k holds
     // X^T row k of the stage, columns [block*CB, block*CB + CB) of the tile.
     // Wave w fills the 1 KB pieces i*NW + w, i = 0 .. LP-1, of each operand.
+    // In the panel-block layout of the buffers every such 1 KB piece is
+    // 1 KB of contiguous global memory: a row-major stage of BT rows is one
+    // piece of a block (stage kt in block column kt), a K-major stage is
+    // BT/CB pieces of KST block rows, one per block column.
     constexpr int GE = 16 / int(sizeof(T));     // elements per granule
     constexpr int KST = KSB / int(sizeof(T));   // contraction indices per stage
-    constexpr int CB = 128 / int(sizeof(T));    // K-major: tile columns per 128-byte LDS row
+    constexpr int CB = 128 / int(sizeof(T));    // columns per 128-byte row (LDS rows and panel blocks)
     constexpr int RPK = 1024 / KSB;             // row-major: LDS rows per 1 KB
+    constexpr int SPB = kBlockRows / KST;       // K-major: stages per block row
+    static_assert(KSB == kBlockBytes && CB == Panel<T>::CB, "stage rows are panel-block rows");
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // The loads go through buffer resources over each operand's matrix
     // buffer (the planner keeps every padded buffer below 2 GB): a per-lane
@@ -842,17 +850,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     // the swizzle reads) do not depend on i; a K-major LDS row R = piece*8 +
     // lane/8 has block R / KST and contraction index R % KST, whose lane part
     // is lane/8.
-    static_assert((NW * RPK) % 16 == 0 && KST % 8 == 0, "load geometry");
+    static_assert((NW * RPK) % 16 == 0 && KST % 8 == 0 && kBlockRows % KST == 0, "load geometry");
     constexpr int ES = int(sizeof(T));
+    constexpr int BLK = kBlockRows * kBlockBytes;  // bytes of a panel block
+    const int rowblk = uni((ld / CB) * BLK);       // bytes of a block row (256 buffer rows)
     uint32_t voff;
     int uP[LP], uQ[LP];  // wave-uniform byte offsets of load i (stage 0)
     int ldsd[LP];        // LDS byte offset of load i inside an operand's stage
     if constexpr (KM) {
         const int l8 = lane >> 3;
-        voff = uint32_t((l8 * ldp + swz_k(l8, lane & 7) * GE) * ES);
+        voff = uint32_t(l8 * kBlockBytes + swz_k(l8, lane & 7) * 16);
     } else {
         const int row = wave_u * RPK + lane / GR;
-        voff = uint32_t(row * ldp * ES + swz_r<GR>(row, lane % GR) * 16);
+        voff = uint32_t(row * kBlockBytes + swz_r<GR>(row, lane % GR) * 16);
     }
 #pragma unroll
     for (int i = 0; i < LP; ++i) {
@@ -860,30 +870,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         ldsd[i] = piece * 1024;
         if constexpr (KM) {
             const int blk = (piece * 8) / KST, k0 = (piece * 8) % KST;
-            uP[i] = uni((k0 * ldp + row0 + blk * CB) * ES);
-            uQ[i] = uni((k0 * ldq + col0 + blk * CB) * ES);
+            uP[i] = uni((row0 / CB + blk) * BLK + k0 * kBlockBytes);
+            uQ[i] = uni((col0 / CB + blk) * BLK + k0 * kBlockBytes);
         } else {
-            uP[i] = uni((row0 + i * NW * RPK) * ldp * ES);
-            uQ[i] = uni((col0 + i * NW * RPK) * ldq * ES);
+            uP[i] = uni((row0 / kBlockRows) * rowblk + ((row0 % kBlockRows) + i * NW * RPK) * kBlockBytes);
+            uQ[i] = uni((col0 / kBlockRows) * rowblk + ((col0 % kBlockRows) + i * NW * RPK) * kBlockBytes);
         }
     }
-    // bytes of each operand's matrix buffer, and between consecutive stages
+    // bytes of each operand's matrix buffer
     const int bytesP = (PHASE == kGram ? np : mp) * ld * ES;
     const int bytesQ = (PHASE == kPoly ? mp : np) * ld * ES;
-    const int stepP = uni(KM ? KST * ldp * ES : KSB);
-    const int stepQ = uni(KM ? KST * ldq * ES : KSB);
+    // byte offset of stage kt from stage 0 (the same for both operands)
+    auto koff = [&](int kt) -> int {
+        if constexpr (KM)
+            return (kt / SPB) * rowblk + (kt % SPB) * (KST * kBlockBytes);
+        else
+            return kt * BLK;
+    };
     // (the resources and wave offsets must live in scalar registers)
     const __amdgpu_buffer_rsrc_t rsP =
         __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(P)), 0, uni(bytesP), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rsQ =
         __builtin_amdgcn_make_buffer_rsrc(uni_ptr(const_cast<T*>(Q)), 0, uni(bytesQ), kRsrcWord3);
     const int KT = K * int(sizeof(T)) / KSB;   // stages along the contraction index
-    auto issue_one = [&](const __amdgpu_buffer_rsrc_t& rs, const int (&u)[LP], int step, int kt, int off) {
+    auto issue_one = [&](const __amdgpu_buffer_rsrc_t& rs, const int (&u)[LP], int kt, int off) {
+        const int ko = koff(kt);
 #pragma unroll
         for (int i = 0; i < LP; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]), 16, int(voff), u[i] + kt * step,
-                0, 0);
+                rs, (__attribute__((address_space(3))) void*)(lds_raw + off + ldsd[i]), 16, int(voff), u[i] + ko, 0, 0);
     };
 
     // Fragment of a 32-column MFMA tile starting at local column c of a
@@ -995,7 +1010,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         const uint32_t lds0 =
             uint32_t(uni(int(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds_raw))));
         auto load_one = [&](bool isP, int kt, int off, int i) {
-            const int so = (isP ? uP[i] + kt * stepP : uQ[i] + kt * stepQ);
+            const int so = (isP ? uP[i] : uQ[i]) + koff(kt);
             if constexpr (KM)
                 dma16_unseen(isP ? wP : wQ, lds0 + uint32_t(off + ldsd[i]), voff, so);
             else
@@ -1090,19 +1105,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             // contraction indices of the stage pair p0 = rows_u / (2*KST): the
             // identity MFMAs of its 8 sub-steps sit at fixed places of the pair
             // (sub-step u of stage 2*p0 + H covers rows 64*H + 16*u: MFMA block
-            // 2*H + u/2, offset 16*(u%2)), under the uniform flags fold_a
-            // (sub-step 3 of the previous stage, run first here) and fold_r (this
+            // 2*H + u/2, offset 16*(u%2)), under the compile-time flags FA
+            // (sub-step 3 of the previous stage, run first here) and FR (this
             // stage's sub-steps 0-2).  FIRST: the tile's stage 0, with no
             // deferred sub-step before it.
-            auto stage = [&](int kt, auto H, bool fold_a, bool fold_r, auto FIRST) {
+            auto stage = [&](int kt, auto H, auto FA, auto FR, auto FIRST) {
                 constexpr int hh = decltype(H)::value;
                 constexpr bool first = decltype(FIRST)::value;
+                constexpr bool fold_a = decltype(FA)::value, fold_r = decltype(FR)::value;
                 const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
                 const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
                 const int oP = sp * OPB, oQ = dg ? oP : (3 + sq) * OPB;
                 const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
                 if constexpr (kFoldAX && !first) {
-                    if (fold_a) {
+                    if constexpr (fold_a) {
                         if constexpr (hh == 0)
                             fold(I3{}, I1{}, fb1);  // sub-step 3 of the second stage of the previous pair
                         else
@@ -1111,7 +1127,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                 }
                 group_k(F0{}, FIRST, fa1, fb1, dg ? 0 : LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
                 if constexpr (kFoldAX && !first)
-                    if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
+                    if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
                 // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
                 // run of LP loads after group 1's reads they overfilled the
                 // texture-address queues (the queue-full counters read about half
@@ -1124,9 +1140,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                         load_one(true, kp, oPn, t - NR);
                 });
                 if constexpr (kFoldAX && first)
-                    if (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
+                    if constexpr (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
                 if constexpr (kFoldAX)
-                    if (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
+                    if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
                 group_k(F0{}, F0{}, fa1, fb1, NR + LP2, NF, [&](int t) {
                     if (t < NR)
                         read_one(t, oP, oQ, 2, fa0, fb0);
@@ -1134,7 +1150,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                         load_one(true, kp, oPn, LP1 + t - NR);
                 });
                 if constexpr (kFoldAX)
-                    if (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
+                    if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
                 group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
                 waitcnt_seen<LP, 0>();
                 __builtin_amdgcn_s_barrier();
@@ -1145,14 +1161,40 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                 __builtin_amdgcn_sched_barrier(0);
             };
             // (KT = K / KST is a multiple of 4: K is a multiple of 256)
-            const int p0 = (row0 + (wave_u / S::WC) * S::WTM) / (2 * KST);  // uniform (wave_u)
-            stage(0, I0{}, false, kFoldAX && p0 == 0, F1{});
-            stage(1, I1{}, kFoldAX && p0 == 0, kFoldAX && p0 == 0, F0{});
-            for (int p = 1; p < KT / 2; ++p) {
-                stage(2 * p, I0{}, kFoldAX && p - 1 == p0, kFoldAX && p == p0, F0{});
-                stage(2 * p + 1, I1{}, kFoldAX && p == p0, kFoldAX && p == p0, F0{});
+            // Plain stage pairs run in loops with no fold and no branch inside;
+            // the fold's pair p0 and the pair after it (whose first stage folds
+            // p0's deferred sub-step 3) are peeled.  Uniform branches around the
+            // fold inside every stage cost about 10% of the update's main loop.
+            auto plain_pairs = [&](int p_begin, int p_end) {
+                for (int p = p_begin; p < p_end; ++p) {
+                    stage(2 * p, I0{}, F0{}, F0{}, F0{});
+                    stage(2 * p + 1, I1{}, F0{}, F0{}, F0{});
+                }
+            };
+            if constexpr (kFoldAX) {
+                const int p0 = uni((row0 + (wave_u / S::WC) * S::WTM) / (2 * KST));
+                if (p0 == 0) {
+                    stage(0, I0{}, F0{}, F1{}, F1{});
+                    stage(1, I1{}, F1{}, F1{}, F0{});
+                } else {
+                    stage(0, I0{}, F0{}, F0{}, F1{});
+                    stage(1, I1{}, F0{}, F0{}, F0{});
+                    plain_pairs(1, p0);
+                    stage(2 * p0, I0{}, F0{}, F1{}, F0{});
+                    stage(2 * p0 + 1, I1{}, F1{}, F1{}, F0{});
+                }
+                if (p0 + 1 < KT / 2) {
+                    stage(2 * p0 + 2, I0{}, F1{}, F0{}, F0{});
+                    stage(2 * p0 + 3, I1{}, F0{}, F0{}, F0{});
+                    plain_pairs(p0 + 2, KT / 2);
+                } else {
+                    fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
+                }
+            } else {
+                stage(0, I0{}, F0{}, F0{}, F1{});
+                stage(1, I1{}, F0{}, F0{}, F0{});
+                plain_pairs(1, KT / 2);
             }
-            if (kFoldAX && p0 == KT / 2 - 1) fold(I3{}, I1{}, fb1);  // the last stage's sub-step 3
             mfmas(fa1, fb1);  // last sub-step of the last stage
             wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
         };
@@ -1181,9 +1223,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         // single stage to arrive.  Past the end the look-ahead re-loads the
         // last stage into released slots no later stage reads.  Inside a
         // stage, the sub-step pipeline of the two-buffer schedule.
-        issue_one(rsP, uP, stepP, 0, 0);
-        issue_one(rsQ, uQ, stepQ, 0, 3 * OPB);
-        issue_one(rsP, uP, stepP, 1 < KT ? 1 : KT - 1, OPB);
+        issue_one(rsP, uP, 0, 0);
+        issue_one(rsQ, uQ, 0, 3 * OPB);
+        issue_one(rsP, uP, 1 < KT ? 1 : KT - 1, OPB);
         wait_vmcnt<LP>();
         stage_barrier();
         u32x4_t fa0[MM], fb0[MN], fa1[MM], fb1[MN];
@@ -1195,8 +1237,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         int sp = 0, sq = 0;  // P and Q slots of stage kt
         for (int kt = 0; kt < KT; ++kt) {
             const int sp2 = sp == 0 ? 2 : sp - 1;  // P slot of stage kt + 2
-            issue_one(rsQ, uQ, stepQ, kt + 1 < KT ? kt + 1 : KT - 1, (3 + (sq ^ 1)) * OPB);
-            issue_one(rsP, uP, stepP, kt + 2 < KT ? kt + 2 : KT - 1, sp2 * OPB);
+            issue_one(rsQ, uQ, kt + 1 < KT ? kt + 1 : KT - 1, (3 + (sq ^ 1)) * OPB);
+            issue_one(rsP, uP, kt + 2 < KT ? kt + 2 : KT - 1, sp2 * OPB);
             mfmas(fa1, fb1);  // last sub-step of the previous stage (zeros on the first)
 #pragma unroll
             for (int u = 1; u < SUBS; ++u) {
@@ -1244,7 +1286,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         // Gram / polynomial: the tile and (off the diagonal) its mirror
         const bool diag = tile.ti == tile.tj;
         T* out = reinterpret_cast<T*>(a.ws + (PHASE == kGram ? d.a_off : d.b_off));
-        const int ldo = ld;
         // Polynomial epilogue operand A, read one MFMA row block ahead along
         // its transposed layout (A is symmetric), where the 4 rows of a lane
         // are 4 consecutive elements.
@@ -1252,7 +1293,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         auto eaddr = [&](int mi, int ni, int q) -> const T* {
             const int rb = row0 + wm * S::WTM + mi * 32 + q * 8 + fhalf * 4;
             const int c = col0 + wn * S::WTN + ni * 32 + frow;
-            return E + int64_t(c) * ld + rb;
+            return E + Panel<T>::off(c, rb, ld);
         };
         typename Vec4<T>::raw ev[2][MN][4];
         if (PHASE == kPoly) {
@@ -1281,9 +1322,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                         v[e] = PHASE == kGram ? acc[mi][ni][q * 4 + e] * (s1 * s1)
                                               : a.cb * Vec4<T>::get(ev[mi & 1][ni][q], e) + a.cc * acc[mi][ni][q * 4 + e];
                     // mirror tile: the 4 rows of this lane are consecutive in column-major
-                    if (!diag) Vec4<T>::store(out + int64_t(c) * ldo + rb, v);
+                    if (!diag) Vec4<T>::store(out + Panel<T>::off(c, rb, ld), v);
                     quad_transpose(v, j);
-                    Vec4<T>::store(out + int64_t(rb + j) * ldo + (c - j), v);
+                    Vec4<T>::store(out + Panel<T>::off(rb + j, c - j, ld), v);
                 }
         }
     }

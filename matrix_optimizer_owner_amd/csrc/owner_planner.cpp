@@ -81,7 +81,7 @@ extern "C" mfsdp_status mfsdp_owner_partition(const mfsdp_tensor* tensors, int64
                 const double m = double(std::min(t.rows, t.cols)), nn = double(std::max(t.rows, t.cols));
                 const uint64_t mp = align_up(uint64_t(std::min(t.rows, t.cols)), kPad);
                 const uint64_t np = align_up(uint64_t(std::max(t.rows, t.cols)), kPad);
-                const uint64_t ld = mp + uint64_t(kLdPad);
+                const uint64_t ld = mp;
                 if (ld * np * uint64_t(es_ns) >= (uint64_t(1) << 31))
                     return fail(MFSDP_ERR_UNSUPPORTED,
                                 "tensor " + std::to_string(i) + ": padded Newton-Schulz buffer of 2 GiB or more");

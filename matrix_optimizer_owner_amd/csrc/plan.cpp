@@ -236,7 +236,7 @@ extern "C" mfsdp_status mfsdp_plan_create(const mfsdp_entry* entries, int64_t n,
             d.np = int32_t(align_up(uint64_t(inf.n), kPad));
             // the kernels address one matrix's Newton-Schulz buffers with
             // 32-bit signed byte offsets
-            d.ld = d.mp + kLdPad;
+            d.ld = d.mp;
             if (uint64_t(d.ld) * uint64_t(d.np) * uint64_t(es) >= (uint64_t(1) << 31)) {
                 delete plan;
                 return fail(MFSDP_ERR_UNSUPPORTED, "entry " + std::to_string(i) +

@@ -93,7 +93,7 @@ int main(int argc, char** argv) {
     regs.push_back({w.off_partials, uint64_t(w.n_k1_blocks) * 4});
     for (int k = 0; k < w.n_mat; ++k) {
         const MatDesc& d = mats[k];
-        CHECK(d.ld == d.mp + kLdPad && (d.ld * es_ns) % 128 == 0, "matrix %d row pitch", k);
+        CHECK(d.ld == d.mp && d.mp % kBlockRows == 0 && d.np % kBlockRows == 0 && (d.ld * es_ns) % kBlockBytes == 0, "matrix %d panel blocks", k);
         const uint64_t xb = uint64_t(d.ld) * d.np * es_ns, ab = uint64_t(d.ld) * d.mp * es_ns;
         regs.push_back({d.x_off[0], xb});
         regs.push_back({d.x_off[1], xb});
