@@ -36,6 +36,7 @@
 // (ds_read_b64_tr_b16), so X is kept only as X^T.  bf16 uses
 // v_mfma_f32_32x32x16_bf16; fp32 uses v_mfma_f32_32x32x2_f32 (four per
 // 8-element granule pair).
+#include <cmath>
 #include <type_traits>
 
 #include "device_util.h"
@@ -54,6 +55,8 @@ struct GemmArgs {
     float* ns_out;
     const float* s;
     float ca, cb, cc;   // quintic coefficients a, b, c
+    float cfold;        // coefficient the 256-tile main loop folds in (update: a; polynomial: b/c)
+    int poly_folded;    // polynomial: the main loop has added (b/c) A (c != 0), so B = c acc
     float lrwd;         // lr * weight_decay
     float lr;
     int first;          // first iteration: scale by s (Gram: s^2)
@@ -578,10 +581,13 @@ __device__ __forceinline__ void update_epilogue_bf16(const f32x16_t (&acc)[Shape
 // offsets), and a quarter-wave's 16-byte reads of one row hit distinct
 // banks.  This replaces an
 // in-register 4 x 4 transpose whose lane-dependent selects cost about 1,500
-// VALU instructions per wave on 256-tiles.  The polynomial's A (for b A) is
-// read along A's transposed layout (A is symmetric), one MFMA row block
-// ahead, where a lane's 4 rows are 4 consecutive elements.
-template <int PHASE, int BT, int NW>
+// VALU instructions per wave on 256-tiles.  FOLDED (polynomial, 256 tiles,
+// c != 0): the main loop has already added (b/c) A, so C = c acc and A is
+// not read here (the polynomial measured 3-4% faster so on the mixed
+// 256-matrix set and the Llama-3-8B share).  Otherwise the polynomial's A
+// (for b A) is read along A's transposed layout (A is symmetric), one MFMA
+// row block ahead, where a lane's 4 rows are 4 consecutive elements.
+template <int PHASE, int BT, int NW, bool FOLDED>
 __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Shape<BT, NW>::MM][Shape<BT, NW>::MN],
                                                         const GemmArgs& a, const MatDesc& d, int row0, int col0, int wm,
                                                         int wn, int frow, int fhalf, float s1, bool diag,
@@ -606,8 +612,9 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
     // mirror rows c .. c + 96 lie in one block row, 32*CB elements apart.
     const uint32_t moff0 = PL::off(col0 + wn * S::WTN + frow, row0 + wm * S::WTM, ld) + uint32_t(fhalf * 4);
     auto moff = [&](int ni) { return moff0 + uint32_t(ni * 32 * PL::CB); };
+    constexpr bool kReadA = PHASE == kPoly && !FOLDED;  // b A added here, not in the main loop
     uint2 ev[2][MN][4];
-    if constexpr (PHASE == kPoly) {
+    if constexpr (kReadA) {
 #pragma unroll
         for (int ni = 0; ni < MN; ++ni)
 #pragma unroll
@@ -616,7 +623,7 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
     if (!diag) __syncthreads();  // every wave is done with the operand stages (block-uniform branch)
 #pragma unroll
     for (int mi = 0; mi < MM; ++mi) {
-        if constexpr (PHASE == kPoly) {
+        if constexpr (kReadA) {
             if (mi + 1 < MM) {
 #pragma unroll
                 for (int ni = 0; ni < MN; ++ni)
@@ -637,6 +644,8 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (PHASE == kGram) {
                         v[e] = acc[mi][ni][q * 4 + e] * s2;
+                    } else if constexpr (FOLDED) {
+                        v[e] = a.cc * acc[mi][ni][q * 4 + e];
                     } else {
                         const uint2 r = ev[mi & 1][ni][q];
                         const uint32_t w = e < 2 ? r.x : r.y;
@@ -779,11 +788,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     constexpr int SUBS = PP::SUBS, GR = PP::GR, OPB = PP::OPB;
     // the Gram's operands are K-major (X^T rows are the contraction index)
     constexpr bool KM = PHASE == kGram;
-    // the update phases of the locked loop add a X inside the main loop
-    // (256 tiles only: the fold's placement assumes each wave's 128 output
-    // rows span one stage pair of the contraction; on 128 tiles the
-    // epilogue adds a X)
-    constexpr bool kFoldAX = Lock4<T, PHASE, BT, NW>::value && BT == 256 && (PHASE == kUpdate || PHASE == kFinal);
+    // On 256 tiles the locked loop adds a multiple of Q's own rows inside the
+    // main loop: a X in the update phases (Q = X^T), (b/c) A in the
+    // polynomial (Q = A, symmetric), so that B = c (A A + (b/c) A) needs no
+    // read of A in its epilogue.  (256 tiles only: the fold's placement
+    // assumes each wave's 128 output rows span one stage pair of the
+    // contraction; on 128 tiles the epilogues add a X and b A.)
+    constexpr bool kFold =
+        Lock4<T, PHASE, BT, NW>::value && BT == 256 && (PHASE == kUpdate || PHASE == kFinal || PHASE == kPoly);
 
     const Tile tile = a.tiles[tile_index];
     const MatDesc d = a.mats[tile.mat];
@@ -1037,42 +1049,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
         };
         using F0 = std::false_type;
         using F1 = std::true_type;
-        // a X folded into the accumulators (update phases): X^T[n][k] sits in
-        // Q's stage slot, so in the sub-steps whose contraction indices k0 ..
-        // k0+15 fall in this wave's output rows m, the MFMA of an identity
-        // fragment with Q's fragments adds a * X[m][n] for those rows.  The
-        // fp32 coefficient a is split exactly into three bf16 terms, a = ahi +
-        // amid + alo (each RNE of what the previous terms leave: ahi holds the
-        // top 8 significant bits, a - ahi has at most 16, a - ahi - amid at
-        // most 8), so every identity product is exact in fp32 and a X enters
-        // the accumulator as three fp32 additions.  Lane (frow, fhalf) of an
-        // identity fragment holds contraction indices 8*fhalf .. 8*fhalf+7 of
-        // row frow: one nonzero when the sub-step starts ro = 16*RO rows into
-        // the 32-row MFMA block BLK.  The fragments are rebuilt at each use (a
-        // few VALU operations) rather than held in registers across the loop.
-        const uint16_t ahi = f32_to_bf16(a.ca);
-        const float ar1 = a.ca - bf16_to_f32(ahi);
+        // f Q[n][m] folded into the accumulators: Q's row n holds the
+        // contraction index k along its stage slot (update: X^T[n][k] = X[k][n];
+        // polynomial: A[n][k] = A[k][n]), so in the sub-steps whose contraction
+        // indices k0 .. k0+15 fall in this wave's output rows m, the MFMA of an
+        // identity fragment with Q's fragments adds f * Q[n][m] for those rows.
+        // The fp32 coefficient f (a.cfold) is split exactly into three bf16
+        // terms, f = ahi + amid + alo (each RNE of what the previous terms
+        // leave: ahi holds the top 8 significant bits, f - ahi has at most 16,
+        // f - ahi - amid at most 8), so every identity product is exact in fp32
+        // and f Q enters the accumulator as three fp32 additions.  Lane (frow,
+        // fhalf) of an identity fragment holds contraction indices 8*fhalf ..
+        // 8*fhalf+7 of row frow: one nonzero when the sub-step starts ro = 16*RO
+        // rows into the 32-row MFMA block BLK.  The fragments are rebuilt at each
+        // use (a few VALU operations) rather than held in registers across the
+        // loop.
+        const uint16_t ahi = f32_to_bf16(a.cfold);
+        const float ar1 = a.cfold - bf16_to_f32(ahi);
         const uint16_t amid = f32_to_bf16(ar1);
         const uint16_t alo = f32_to_bf16(ar1 - bf16_to_f32(amid));
         auto fold = [&](auto blk, auto ro, const u32x4_t (&fb)[MN]) {
           // (instantiated only where the fold is used: 256-tiles, MM = 4)
-          if constexpr (kFoldAX) {
+          if constexpr (kFold) {
             int t = frow - 16 * decltype(ro)::value - 8 * fhalf;
             asm volatile("" : "+v"(t));  // keeps the fragments out of loop-invariant hoisting
-            u32x4_t ih, im, il;
+            // one identity fragment at a time (four registers, not twelve)
+            const uint16_t terms[3] = {ahi, amid, alo};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const bool on = t >= 0 && t < 8 && (t >> 1) == w;
-                ih[w] = on ? uint32_t(ahi) << (16 * (t & 1)) : 0u;
-                im[w] = on ? uint32_t(amid) << (16 * (t & 1)) : 0u;
-                il[w] = on ? uint32_t(alo) << (16 * (t & 1)) : 0u;
+            for (int h = 0; h < 3; ++h) {
+                u32x4_t id;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const bool on = t >= 0 && t < 8 && (t >> 1) == w;
+                    id[w] = on ? uint32_t(terms[h]) << (16 * (t & 1)) : 0u;
+                }
+#pragma unroll
+                for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], id, fb[jj]);
             }
-#pragma unroll
-            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], ih, fb[jj]);
-#pragma unroll
-            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], im, fb[jj]);
-#pragma unroll
-            for (int jj = 0; jj < MN; ++jj) Mfma<T>::step(acc[decltype(blk)::value][jj], il, fb[jj]);
             __builtin_amdgcn_sched_barrier(0);
           }
         };
@@ -1117,7 +1130,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                 const int kq = kt + 1 < KT ? kt + 1 : KT - 1, kp = kt + 2 < KT ? kt + 2 : KT - 1;
                 const int oP = sp * OPB, oQ = dg ? oP : (3 + sq) * OPB;
                 const int oQn = (3 + (sq ^ 1)) * OPB, oPn = sp2 * OPB;
-                if constexpr (kFoldAX && !first) {
+                if constexpr (kFold && !first) {
                     if constexpr (fold_a) {
                         if constexpr (hh == 0)
                             fold(I3{}, I1{}, fb1);  // sub-step 3 of the second stage of the previous pair
@@ -1126,7 +1139,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     }
                 }
                 group_k(F0{}, FIRST, fa1, fb1, dg ? 0 : LP, NF, [&](int t) { load_one(false, kq, oQn, t); });
-                if constexpr (kFoldAX && !first)
+                if constexpr (kFold && !first)
                     if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I0{}, fb0);
                 // P loads (stage kt + 2) in groups 1 and 2, half each: issued as one
                 // run of LP loads after group 1's reads they overfilled the
@@ -1139,9 +1152,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     else
                         load_one(true, kp, oPn, t - NR);
                 });
-                if constexpr (kFoldAX && first)
+                if constexpr (kFold && first)
                     if constexpr (fold_r) fold(I0{}, I0{}, fb0);  // after the accumulators started
-                if constexpr (kFoldAX)
+                if constexpr (kFold)
                     if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh>{}, I1{}, fb1);
                 group_k(F0{}, F0{}, fa1, fb1, NR + LP2, NF, [&](int t) {
                     if (t < NR)
@@ -1149,7 +1162,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     else
                         load_one(true, kp, oPn, LP1 + t - NR);
                 });
-                if constexpr (kFoldAX)
+                if constexpr (kFold)
                     if constexpr (fold_r) fold(std::integral_constant<int, 2 * hh + 1>{}, I0{}, fb0);
                 group_k(F0{}, F0{}, fa0, fb0, NR, NF / 2, [&](int t) { read_one(t, oP, oQ, 3, fa1, fb1); });
                 waitcnt_seen<LP, 0>();
@@ -1163,15 +1176,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             // (KT = K / KST is a multiple of 4: K is a multiple of 256)
             // Plain stage pairs run in loops with no fold and no branch inside;
             // the fold's pair p0 and the pair after it (whose first stage folds
-            // p0's deferred sub-step 3) are peeled.  Uniform branches around the
-            // fold inside every stage cost about 10% of the update's main loop.
+            // p0's deferred sub-step 3) are peeled.  (Uniform branches around
+            // the fold inside every stage made the update about 2% slower.)
             auto plain_pairs = [&](int p_begin, int p_end) {
                 for (int p = p_begin; p < p_end; ++p) {
                     stage(2 * p, I0{}, F0{}, F0{}, F0{});
                     stage(2 * p + 1, I1{}, F0{}, F0{}, F0{});
                 }
             };
-            if constexpr (kFoldAX) {
+            if constexpr (kFold) {
                 const int p0 = uni((row0 + (wave_u / S::WC) * S::WTM) / (2 * KST));
                 if (p0 == 0) {
                     stage(0, I0{}, F0{}, F1{}, F1{});
@@ -1198,13 +1211,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
             mfmas(fa1, fb1);  // last sub-step of the last stage
             wait_vmcnt<0>();  // the tail's re-loads land before LDS is reused or released
         };
-        // Not for the Gram on 256-tiles: there a diagonal tile would finish
-        // early (K = n is long) and its CU would start the next tile group
-        // while the rest of its group still streams the strips they share,
-        // so the 32 tiles an XCD runs together drift apart and re-fetch
-        // evicted strips.  On the mixed 256-matrix set that took the Gram's
-        // L2 misses from 28 to 65 GB per launch and its time up 5%.
-        if constexpr (PHASE == kPoly || (PHASE == kGram && BT == 128)) {
+        // 128 tiles only.  Not for the Gram on 256-tiles: there a diagonal
+        // tile would finish early (K = n is long) and its CU would start the
+        // next tile group while the rest of its group still streams the
+        // strips they share, so the 32 tiles an XCD runs together drift apart
+        // and re-fetch evicted strips.  On the mixed 256-matrix set that took
+        // the Gram's L2 misses from 28 to 65 GB per launch and its time up 5%.
+        // Not for the polynomial on 256-tiles either: with the fold the
+        // second instantiation of the loop made the kernel spill registers,
+        // and without it the polynomial measured as fast.
+        if constexpr ((PHASE == kPoly || PHASE == kGram) && BT == 128) {
             if (uni(int(tile.ti) - int(tile.tj)) == 0)
                 run(std::true_type{});
             else
@@ -1268,19 +1284,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
     const float s1 = a.first ? a.s[tile.mat] : 1.f;
     const int j = frow & 3;
     if constexpr (PHASE == kFinal) {
-        final_update<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
+        final_update<T, BT, NW, !kFold>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin,
                                 reinterpret_cast<float*>(lds_raw));
         return;
     } else if constexpr (PHASE == kUpdate) {
         T* XTout = reinterpret_cast<T*>(a.ws + (a.x_out ? d.x_off[1] : d.x_off[0]));
-        if constexpr (kFoldAX && sizeof(T) == 2)
+        if constexpr (kFold && sizeof(T) == 2)
             update_epilogue_bf16<BT, NW>(acc, d, row0, col0, wm, wn, frow, fhalf, s1, XTout, lds_raw);
         else
-            update_epilogue<T, BT, NW, !kFoldAX>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, XTout, lds_raw);
+            update_epilogue<T, BT, NW, !kFold>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, XTin, XTout, lds_raw);
         return;
     } else if constexpr (sizeof(T) == 2) {
-        gram_poly_epilogue_bf16<PHASE, BT, NW>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1,
-                                                uni(int(tile.ti) - int(tile.tj)) == 0, lds_raw);
+        const bool diag = uni(int(tile.ti) - int(tile.tj)) == 0;
+        if (kFold && PHASE == kPoly && a.poly_folded)
+            gram_poly_epilogue_bf16<PHASE, BT, NW, kFold>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, diag, lds_raw);
+        else
+            gram_poly_epilogue_bf16<PHASE, BT, NW, false>(acc, a, d, row0, col0, wm, wn, frow, fhalf, s1, diag, lds_raw);
         return;
     } else {
         // Gram / polynomial: the tile and (off the diagonal) its mirror
@@ -1370,6 +1389,14 @@ hipError_t launch_phase(const WorkspaceMap& map, const mfsdp_hparams& hp, int it
     a.ca = hp.ns_a;
     a.cb = hp.ns_b;
     a.cc = hp.ns_c;
+    // The polynomial's 256-tile main loop adds (b/c) A, and its epilogue
+    // scales by c: B = c A A + (c (b/c)) A, where c (b/c) = b up to one fp32
+    // rounding.  With c = 0 (or b/c not finite) the loop adds 0 A and the
+    // epilogue forms b A + c A A from A.
+    const float bc = hp.ns_c != 0.f ? hp.ns_b / hp.ns_c : 0.f;
+    const bool poly_fold = hp.ns_c != 0.f && std::isfinite(bc);
+    a.cfold = phase == 1 ? (poly_fold ? bc : 0.f) : hp.ns_a;
+    a.poly_folded = phase == 1 && poly_fold;
     a.lrwd = float(double(hp.lr) * double(hp.weight_decay));
     a.lr = hp.lr;
     a.first = iter == 1 && phase != 1;  // the polynomial sees an already normalised A
