@@ -680,38 +680,6 @@ __device__ __forceinline__ void gram_poly_epilogue_bf16(const f32x16_t (&acc)[Sh
     }
 }
 
-// Scheduling groups for one stage of the main loop (bf16), in program order:
-// the stage's direct-to-LDS loads and the previous stage's deferred last
-// sub-step of MFMAs, interleaved with sub-step 1's fragment reads; then for
-// each further sub-step its MFMAs interleaved with the next fragment reads;
-// then the MFMAs of the second-to-last sub-step.  NDS is the number of LDS
-// read instructions per sub-step.
-template <int NMF, int NDS, int NVM, int SUBS>
-__device__ __forceinline__ void stage_schedule() {
-    constexpr int mf = NMF / NDS > 0 ? NMF / NDS : 1;
-    constexpr int groups = NMF / mf < NDS ? NMF / mf : NDS;  // groups that carry an MFMA
-    constexpr int vm = NVM / NDS;
-    constexpr int mf_tail = NMF - mf * groups, vm_tail = NVM - vm * NDS;
-#pragma unroll
-    for (int t = 0; t < NDS; ++t) {
-        if (t < groups) __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);  // MFMA
-        if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-    if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
-    if constexpr (vm_tail > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm_tail, 0);
-#pragma unroll
-    for (int r = 0; r < SUBS - 2; ++r) {
-#pragma unroll
-        for (int t = 0; t < NDS; ++t) {
-            if (t < groups) __builtin_amdgcn_sched_group_barrier(0x008, mf, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if constexpr (mf_tail > 0) __builtin_amdgcn_sched_group_barrier(0x008, mf_tail, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -1266,7 +1234,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile_index, uin
                     mfmas(fa1, fb1);
                 }
             }
-            if constexpr (sizeof(T) == 2) stage_schedule<MM * MN, (KM ? 2 : 1) * (MM + MN), 2 * LP, SUBS>();
             wait_vmcnt<LP>();
             stage_barrier();
             sp = sp == 2 ? 0 : sp + 1;

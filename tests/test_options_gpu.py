@@ -106,10 +106,11 @@ def test_ragged_shapes_on_256_tiles(precision):
 
 @pytest.mark.parametrize("coeffs", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
 def test_other_coefficients_on_256_tiles(coeffs):
-    """Other iteration coefficients on the 256-tile bf16 kernels (the cubic
-    iteration, c = 0, and a second quintic): the folded a X and the
-    polynomial's b A + c A^2 epilogue take the coefficients from the
-    parameters, and the oracle runs the same coefficients."""
+    """Other iteration coefficients on the 256-tile bf16 kernels, and the
+    oracle with the same coefficients.  The cubic iteration (c = 0) takes the
+    polynomial's unfolded path (the main loop folds 0 A, the epilogue forms
+    b A + c A^2 from A); the second quintic folds (b/c) A = -3 A into the main
+    loop and scales by c.  The update folds a X either way."""
     a, b, c = coeffs
     _steps(W.small_ragged(precision=0), 1, {"ns_a": a, "ns_b": b, "ns_c": c, "ns_tile": 256}, label=f"coef{a},{b},{c}")
 
