@@ -175,7 +175,7 @@ def cpu_baseline_tail(wl, hp, budget_s: float, cores: int):
 # for the kernel sources they were taken with.
 TRAFFIC = {
     # (workload, precision, phase): (sources sha256[:16], fetch bytes, write bytes)
-    ("mixed-256-stress", "bf16", "update"): ("c0aaf8b424d4412b", 53031242560, 9145679872),
+    ("mixed-256-stress", "bf16", "update"): ("4de108779a05685d", 49695033376, 9145679872),
 }
 TRAFFIC_SOURCES = ("matrix_optimizer_owner_amd/csrc/ns_gemm.hip", "matrix_optimizer_owner_amd/csrc/plan.cpp",
                    "matrix_optimizer_owner_amd/csrc/layout.h")

@@ -2,14 +2,14 @@
 //
 // Muon orthogonalises the momentum-smoothed update with Newton-Schulz
 // (MatrixFSDP, arXiv 2607.05895, Abstract).  One quintic iteration on the
-// wide X (m x n, m <= n, row-major) is three products C = P Q^T:
+// wide X (m x n, m <= n) is three products C = P Q^T:
 //
 //   Gram     A = X X^T           P = Q = X, read K-major from X^T (its rows
 //                                are the contraction index); K = n; upper
 //                                tiles only, each stored with its mirror
 //   poly     B = b A + c A A^T   P = Q = A; K = m; upper tiles, mirrored
 //                                (A is symmetric, so A A = A A^T)
-//   update   X' = a X + B X      P = B, Q = X^T (both row-major along the
+//   update   X' = a X + B X      P = B, Q = X^T (both read along the
 //                                contraction); all tiles; X'^T goes to the
 //                                other X^T buffer
 //   final    the last update writes W <- W (1 - lr wd) - lr*scale*O instead
