@@ -251,8 +251,8 @@ mfsdp_status mfsdp_plan_destroy(mfsdp_plan_t plan);
 /* ---- Owner planner (host only) ----
  *
  * "MatrixFSDP" (arXiv 2607.05895), Abstract: a balance-aware owner planner
- * decides which data-parallel rank owns each whole 2D weight, and the
- * non-matrix tensors are packed into tail owners.  The pages name the
+ * decides which data-parallel rank owns each whole 2D weight, and tensors
+ * that are not matrices are grouped onto a few tail owners.  The pages name the
  * planner only; this one reads "balance-aware" as: every tensor goes whole
  * to one owner, an owner's step time is the sum of its tensors' costs, and
  * the plan minimises the largest owner time under a per-owner memory cap.

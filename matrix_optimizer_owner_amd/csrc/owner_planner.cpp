@@ -3,8 +3,8 @@
 //
 // "MatrixFSDP: Communication-Free Matrix Optimizers Under ZeRO-3 Parameter
 // Sharding" (arXiv 2607.05895), Abstract: one data-parallel rank owns each
-// whole 2D weight, the non-matrix tensors are packed into tail owners, and a
-// balance-aware owner planner makes that placement.  The pages give no
+// whole 2D weight, tensors that are not matrices are grouped onto a few
+// tail owners, and a balance-aware owner planner makes that placement.  The pages give no
 // algorithm; the cost and memory model and the objective are stated in
 // mfsdp.h (mfsdp_owner_partition).  The memory model follows the layout
 // mfsdp_plan_create gives an owner's table.
