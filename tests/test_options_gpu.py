@@ -115,11 +115,14 @@ def test_other_coefficients_on_256_tiles(coeffs):
     _steps(W.small_ragged(precision=0), 1, {"ns_a": a, "ns_b": b, "ns_c": c, "ns_tile": 256}, label=f"coef{a},{b},{c}")
 
 
-def test_bitwise_deterministic():
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_bitwise_deterministic(cfg):
     """Two runs of the same step from the same state give identical bytes
     (fixed-order Sigma u^2, no float atomics); the second run reuses the
-    descriptors already resident in the workspace."""
-    wl = W.config(1)
+    descriptors already resident in the workspace.  The GPT-2 buffer runs
+    its Gram and polynomial on 128-tiles, the Llama-3-8B share on 256-tiles
+    (with the polynomial's folded (b/c) A)."""
+    wl = W.config(cfg)
     run = DeviceRun(wl)
     try:
         run.fill(1, params_too=True)
